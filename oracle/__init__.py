@@ -1,0 +1,6 @@
+"""Float64 CPU oracle for the selective scan -- TEST INFRASTRUCTURE ONLY.
+
+Only tests, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline``
+leg may import this package.  The product path never does.
+"""
+from .oracle import build, scan, state_update, oracle_lib_path  # noqa: F401
