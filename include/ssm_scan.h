@@ -1,0 +1,127 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective-scan library.
+ *
+ * Two operations, both defined by the sequential loop of the SelectiveSSMLayer
+ * in "Linear Attention vs Softmax Attention: Can RWKV or Mamba Replace
+ * Transformers?" (shyankdev.com), section "Implementation", with the step size
+ * Delta = softplus(parameter + projection) of "State Space Models in Large
+ * Language Models" (llms.blog), section "Dynamic Parameterization":
+ *
+ *   for each sequence b and channel d, with state h[0..N) (float32):
+ *     Delta_t = softplus(delta[b,t,d] + delta_bias[d])   (or delta+bias if the flag is 0)
+ *     h[n]    = exp(Delta_t * A[d,n]) * h[n] + Delta_t * B[b,t,n] * x[b,t,d]
+ *     y       = sum_n C[b,t,n] * h[n] + D_skip[d] * x[b,t,d]
+ *     out[b,t,d] = z ? y * z*sigmoid(z) : y
+ *
+ * ssm_scan_fwd runs it over a whole sequence (the fused "hardware-aware scan"
+ * of llms.blog, section "The Hardware-Aware Parallel Associative Scan": inputs
+ * read once, only outputs written, no (b,L,D,N) intermediate in memory);
+ * ssm_state_update is the one-token recurrent step used in decoding (same
+ * page, section "Discretization", recurrent view), updating the state in place.
+ *
+ * Conventions common to every entry point:
+ *   - Pointers named as tensors are DEVICE pointers (hipMalloc'd or torch
+ *     device memory) on the current HIP device; all tensors are contiguous and
+ *     row-major in the layouts given below.
+ *   - "act" tensors (x, delta, z, B, C, out) have the element type `dtype`
+ *     (SSM_DTYPE_F32 or SSM_DTYPE_BF16); A, D_skip, delta_bias and every state
+ *     tensor are always float32.  Arithmetic and the state are float32; bf16
+ *     outputs are rounded to nearest even.
+ *   - The caller owns every buffer.  The library allocates no device memory,
+ *     keeps no per-call state and never synchronises: work is enqueued on
+ *     `stream` (NULL = the default stream) and the call returns at once.
+ *     Results are valid once the caller orders later work after the stream.
+ *   - Argument errors are detected on the host before anything is enqueued:
+ *     the call returns a negative ssm_status_t, leaves every output untouched
+ *     and records a message for ssm_last_error().  A failed launch returns
+ *     SSM_ERR_HIP.  Faults during execution surface at the caller's next
+ *     synchronisation, as for any HIP kernel.
+ *   - Alignment: act tensors must be aligned to their element size; A, D_skip,
+ *     delta_bias to 4 bytes; B and C to 4 bytes; state tensors to 16 bytes.
+ *   - Outputs may not overlap inputs, except that last_state may be the same
+ *     buffer as initial_state (resume in place).
+ *   - Not thread-hostile: concurrent calls on different streams are fine.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_SCAN_ABI_VERSION 1
+
+typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  SSM_ERR_SHAPE = -2,       /* a size is negative / zero where it may not be, or too large */
+  SSM_ERR_UNSUPPORTED = -3, /* dstate outside [1, 64], unknown dtype, flag not 0/1 */
+  SSM_ERR_ALIGN = -4,       /* a pointer violates the alignment rules above        */
+  SSM_ERR_ALIAS = -5,       /* an output overlaps an input                         */
+  SSM_ERR_WORKSPACE = -6,   /* workspace smaller than ssm_scan_fwd_workspace_bytes */
+  SSM_ERR_HIP = -7          /* the HIP runtime refused a launch or query           */
+} ssm_status_t;
+
+/*
+ * Forward selective scan over whole sequences.
+ *   x, delta, z, out : (batch, seqlen, dim) act     -- delta is the raw step
+ *                      parameter, before softplus; z may be NULL (no gate)
+ *   delta_bias       : (dim) float32 or NULL (= 0)
+ *   delta_softplus   : 1 = Delta = softplus(delta + bias), 0 = Delta = delta + bias
+ *   A                : (dim, dstate) float32 (negative for a decaying state)
+ *   B, C             : (batch, seqlen, dstate) act, shared by all channels
+ *   D_skip           : (dim) float32 or NULL (no skip term)
+ *   initial_state    : (batch, dim, dstate) float32 or NULL (= zeros)
+ *   last_state       : (batch, dim, dstate) float32 or NULL; receives h after
+ *                      the last token
+ *   batch, dim >= 1; seqlen >= 0 (seqlen == 0 only copies the initial state
+ *   into last_state); 1 <= dstate <= 64.
+ *   workspace        : device scratch of at least
+ *                      ssm_scan_fwd_workspace_bytes(...) bytes, 256-byte
+ *                      aligned; may be NULL when that size is 0.  Its contents
+ *                      need no initialisation and are garbage afterwards.
+ * The result does not depend on how the work is partitioned beyond float32
+ * rounding order, and is bitwise reproducible run to run on one device.
+ */
+int ssm_scan_fwd(const void* x, const void* delta, const float* delta_bias, int delta_softplus,
+                 const float* A, const void* B, const void* C, const float* D_skip,
+                 const void* z, void* out, float* last_state, const float* initial_state,
+                 int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int dtype,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace size the call above needs for these sizes on the current device
+ * (0 when none is needed).  Never fails; returns 0 for invalid sizes. */
+size_t ssm_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                    int dtype);
+
+/*
+ * One decoding step for `batch` sequences: the recurrence above with one token.
+ *   state       : (batch, dim, dstate) float32, read and overwritten in place
+ *   x, delta, z, out : (batch, dim) act; z may be NULL
+ *   B, C        : (batch, dstate) act
+ *   delta_bias, D_skip : (dim) float32 or NULL;  A : (dim, dstate) float32
+ * Equivalent to ssm_scan_fwd with seqlen = 1 and initial_state = last_state =
+ * state.
+ */
+int ssm_state_update(float* state, const void* x, const void* delta, const float* delta_bias,
+                     int delta_softplus, const float* A, const void* B, const void* C,
+                     const float* D_skip, const void* z, void* out,
+                     int64_t batch, int64_t dim, int64_t dstate, int dtype, hipStream_t stream);
+
+/* Message for the most recent non-OK status returned on the calling thread
+ * ("" if none).  The pointer stays valid until the next call on that thread. */
+const char* ssm_last_error(void);
+
+/* SSM_SCAN_ABI_VERSION of the loaded library. */
+int ssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,179 @@
+"""Thin Python binding of the C ABI in include/ssm_scan.h.
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+libssm_scan.so.  PyTorch supplies device memory and the current HIP stream.
+The functions keep the C names.  If the library is missing the import of the
+first call fails loudly; there is no fallback implementation.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssm_scan.so")
+
+SSM_DTYPE_F32 = 0
+SSM_DTYPE_BF16 = 1
+_DTYPES = {torch.float32: SSM_DTYPE_F32, torch.bfloat16: SSM_DTYPE_BF16}
+
+STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL", -2: "SSM_ERR_SHAPE", -3: "SSM_ERR_UNSUPPORTED",
+          -4: "SSM_ERR_ALIGN", -5: "SSM_ERR_ALIAS", -6: "SSM_ERR_WORKSPACE", -7: "SSM_ERR_HIP"}
+
+EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_state_update", "ssm_last_error",
+           "ssm_abi_version")
+
+
+class SsmError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s (%d): %s" % (STATUS.get(code, "?"), code, msg))
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libssm_scan.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError("libssm_scan.so not found at %s: build it first "
+                          "(python -c 'import __graft_entry__ as g; g.build()')" % path)
+    lib = ctypes.CDLL(path)
+    P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.ssm_scan_fwd.argtypes = [P, P, P, I, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I, P, SZ, P]
+    lib.ssm_scan_fwd.restype = I
+    lib.ssm_scan_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
+    lib.ssm_scan_fwd_workspace_bytes.restype = SZ
+    lib.ssm_state_update.argtypes = [P, P, P, P, I, P, P, P, P, P, P, I64, I64, I64, I, P]
+    lib.ssm_state_update.restype = I
+    lib.ssm_last_error.argtypes = []
+    lib.ssm_last_error.restype = ctypes.c_char_p
+    lib.ssm_abi_version.argtypes = []
+    lib.ssm_abi_version.restype = I
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _raise(code):
+    msg = load_library().ssm_last_error().decode(errors="replace")
+    raise SsmError(code, msg)
+
+
+def ssm_abi_version():
+    return load_library().ssm_abi_version()
+
+
+def ssm_last_error():
+    return load_library().ssm_last_error().decode(errors="replace")
+
+
+def ssm_scan_fwd_workspace_bytes(batch, seqlen, dim, dstate, dtype=torch.bfloat16):
+    return int(load_library().ssm_scan_fwd_workspace_bytes(batch, seqlen, dim, dstate, _DTYPES[dtype]))
+
+
+def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                 initial_state=None, return_last_state=False, out=None, last_state=None,
+                 workspace=None, stream=None):
+    """Selective scan forward over (batch, seqlen, dim) activations.
+
+    Returns ``out`` (same dtype as x), or ``(out, last_state)`` when
+    ``return_last_state`` is set (or a ``last_state`` buffer is passed).
+    """
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, seqlen, dim)")
+    batch, L, dim = x.shape
+    if A.dim() != 2:
+        raise ValueError("A must be (dim, dstate)")
+    N = A.shape[1]
+    dev, dt = x.device, x.dtype
+    if dt not in _DTYPES:
+        raise TypeError("activations must be float32 or bfloat16, got %s" % dt)
+    _check(x, "x", (batch, L, dim), dt, dev)
+    _check(delta, "delta", (batch, L, dim), dt, dev)
+    _check(z, "z", (batch, L, dim), dt, dev, optional=True)
+    _check(B, "B", (batch, L, N), dt, dev)
+    _check(C, "C", (batch, L, N), dt, dev)
+    _check(A, "A", (dim, N), torch.float32, dev)
+    _check(D, "D", (dim,), torch.float32, dev, optional=True)
+    _check(delta_bias, "delta_bias", (dim,), torch.float32, dev, optional=True)
+    _check(initial_state, "initial_state", (batch, dim, N), torch.float32, dev, optional=True)
+    if out is None:
+        out = torch.empty((batch, L, dim), dtype=dt, device=dev)
+    _check(out, "out", (batch, L, dim), dt, dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _check(last_state, "last_state", (batch, dim, N), torch.float32, dev, optional=True)
+    need = int(lib.ssm_scan_fwd_workspace_bytes(batch, L, dim, N, _DTYPES[dt]))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(A),
+                          _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(out), _ptr(last_state),
+                          _ptr(initial_state), batch, L, dim, N, _DTYPES[dt], _ptr(workspace),
+                          ws_bytes, ctypes.c_void_p(stream))
+    if rc != 0:
+        _raise(rc)
+    if last_state is not None:
+        return out, last_state
+    return out
+
+
+def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None,
+                     delta_softplus=True, out=None, stream=None):
+    """One decode step: ``state`` (batch, dim, dstate) float32 is updated in
+    place; returns ``out`` (batch, dim) in x's dtype."""
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be (batch, dim)")
+    batch, dim = x.shape
+    N = A.shape[1]
+    dev, dt = x.device, x.dtype
+    if dt not in _DTYPES:
+        raise TypeError("activations must be float32 or bfloat16, got %s" % dt)
+    _check(state, "state", (batch, dim, N), torch.float32, dev)
+    _check(x, "x", (batch, dim), dt, dev)
+    _check(delta, "delta", (batch, dim), dt, dev)
+    _check(z, "z", (batch, dim), dt, dev, optional=True)
+    _check(B, "B", (batch, N), dt, dev)
+    _check(C, "C", (batch, N), dt, dev)
+    _check(A, "A", (dim, N), torch.float32, dev)
+    _check(D, "D", (dim,), torch.float32, dev, optional=True)
+    _check(delta_bias, "delta_bias", (dim,), torch.float32, dev, optional=True)
+    if out is None:
+        out = torch.empty((batch, dim), dtype=dt, device=dev)
+    _check(out, "out", (batch, dim), dt, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssm_state_update(_ptr(state), _ptr(x), _ptr(delta), _ptr(delta_bias),
+                              int(bool(delta_softplus)), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                              _ptr(out), batch, dim, N, _DTYPES[dt], ctypes.c_void_p(stream))
+    if rc != 0:
+        _raise(rc)
+    return out

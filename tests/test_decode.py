@@ -1,0 +1,121 @@
+"""GPU parity of the one-token state update (decode) with the oracle, and the
+recurrent view equals the full scan (chained steps == one forward pass)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from selective_state_space_31_amd import ssm_scan_fwd, ssm_state_update
+from selective_state_space_31_amd.workloads import CONFIGS, make_decode_tokens, make_problem
+from tests._helpers import TOL, assert_close, oracle_for, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("N", [16, 4, 8, 32, 64, 1, 3, 12])
+@pytest.mark.parametrize("flags", [dict(), dict(gate=False, with_D=False, with_bias=False),
+                                   dict(delta_softplus=False)], ids=["all", "bare", "nosoftplus"])
+def test_one_step_matches_oracle(N, dtype, flags):
+    print("case: decode N=%d %s %s" % (N, dtype, flags), flush=True)
+    kw = dict(gate=True)
+    kw.update(flags)
+    p = make_problem(5, 1, 200, N, dtype=dtype, seed=20 + N, device=DEV, initial_state=True, **kw)
+    if not p.delta_softplus:
+        # keep Delta = delta + bias positive and moderate without softplus
+        p.delta = (p.delta.float().abs() * 0.1).to(p.delta.dtype)
+        p.delta_bias = torch.full_like(p.delta_bias, 0.01)
+    state = p.h0.clone()
+    out = ssm_state_update(state, p.x[:, 0], p.delta[:, 0], p.A, p.B[:, 0], p.C[:, 0], D=p.D,
+                           z=None if p.z is None else p.z[:, 0], delta_bias=p.delta_bias,
+                           delta_softplus=p.delta_softplus)
+    torch.cuda.synchronize()
+    ref, ref_last = oracle_for(p)
+    rtol, atol = TOL[dtype]
+    assert_close(to_np(out), ref[:, 0], rtol, atol, "decode out")
+    assert_close(to_np(state), ref_last, rtol, atol, "decode state")
+
+
+def test_one_step_equals_forward_with_L1():
+    p = make_problem(3, 1, 130, 16, dtype="fp32", seed=31, device=DEV, initial_state=True)
+    state = p.h0.clone()
+    o1 = ssm_state_update(state, p.x[:, 0], p.delta[:, 0], p.A, p.B[:, 0], p.C[:, 0], D=p.D,
+                          z=p.z[:, 0], delta_bias=p.delta_bias)
+    o2, last = ssm_scan_fwd(**p.tensors(), return_last_state=True)
+    torch.cuda.synchronize()
+    assert_close(to_np(o1), to_np(o2[:, 0]), *TOL["fp32"], what="decode vs fwd L=1")
+    assert_close(to_np(state), to_np(last), *TOL["fp32"], what="state vs last_state")
+
+
+def chained(tok, steps):
+    state = tok["state0"].clone()
+    outs = []
+    for s in range(steps):
+        outs.append(ssm_state_update(state, tok["x"][s], tok["delta"][s], tok["A"], tok["B"][s],
+                                     tok["C"][s], D=tok["D"], z=tok["z"][s],
+                                     delta_bias=tok["delta_bias"]))
+    return torch.stack(outs), state
+
+
+def test_chain_equals_full_scan_small():
+    steps, batch, dim, N = 40, 3, 96, 16
+    tok = make_decode_tokens(steps, batch, dim, N, seed=5, device=DEV, engine="numpy")
+    outs, state = chained(tok, steps)
+    tr = lambda t: t.transpose(0, 1).contiguous()
+    fo, fl = ssm_scan_fwd(tr(tok["x"]), tr(tok["delta"]), tok["A"], tr(tok["B"]), tr(tok["C"]),
+                          D=tok["D"], z=tr(tok["z"]), delta_bias=tok["delta_bias"],
+                          initial_state=tok["state0"], return_last_state=True)
+    torch.cuda.synchronize()
+    assert_close(to_np(tr(outs)), to_np(fo), *TOL["fp32"], what="chain vs fwd out")
+    assert_close(to_np(state), to_np(fl), *TOL["fp32"], what="chain vs fwd state")
+    ref, ref_last = oracle.scan(*(tr(tok[k]).cpu().numpy() for k in ("x", "delta")),
+                                tok["A"].cpu().numpy(), tr(tok["B"]).cpu().numpy(),
+                                tr(tok["C"]).cpu().numpy(), D=tok["D"].cpu().numpy(),
+                                z=tr(tok["z"]).cpu().numpy(),
+                                delta_bias=tok["delta_bias"].cpu().numpy(),
+                                h0=tok["state0"].cpu().numpy())
+    assert_close(to_np(tr(outs)), ref, *TOL["fp32"], what="chain vs oracle")
+    assert_close(to_np(state), ref_last, *TOL["fp32"], what="chain state vs oracle")
+
+
+def test_config_decode_fp32_1024_steps():
+    """Decode workload at full size: 256 sequences x 5120 channels x N=16,
+    1024 chained steps from a N(0,1) state.  Checked against the oracle's
+    full scan of the same tokens on sampled (sequence, channel) pairs (every
+    step and the final state), and against the GPU forward scan of the same
+    tokens on every element.  Each GPU path is within (rtol, atol) of the
+    exact result, so the two are compared with twice that budget."""
+    c = CONFIGS["decode_fp32"]
+    steps, batch, dim, N = c["steps"], c["batch"], c["dim"], c["dstate"]
+    print("case: decode_fp32 full", flush=True)
+    tok = make_decode_tokens(steps, batch, dim, N, seed=0, device=DEV, engine="torch_cuda")
+    outs, state = chained(tok, steps)
+    torch.cuda.synchronize()
+    rtol, atol = TOL["fp32"]
+    # oracle (full scan from state0) on sampled pairs
+    rng = np.random.default_rng(4)
+    bs = torch.from_numpy(np.array([0, 77, 150, batch - 1])).to(DEV)
+    ds = torch.from_numpy(np.unique(np.concatenate([[0, dim - 1], rng.choice(dim, 62, replace=False)]))).to(DEV)
+    sub = lambda t: t[:, bs][..., ds].transpose(0, 1).contiguous().cpu().numpy()
+    ref, ref_last = oracle.scan(sub(tok["x"]), sub(tok["delta"]), tok["A"][ds].cpu().numpy(),
+                                tok["B"][:, bs].transpose(0, 1).contiguous().cpu().numpy(),
+                                tok["C"][:, bs].transpose(0, 1).contiguous().cpu().numpy(),
+                                D=tok["D"][ds].cpu().numpy(), z=sub(tok["z"]),
+                                delta_bias=tok["delta_bias"][ds].cpu().numpy(),
+                                h0=tok["state0"][bs][:, ds].cpu().numpy())
+    got = outs[:, bs][..., ds].transpose(0, 1)
+    assert_close(to_np(got), ref, rtol, atol, "decode chain vs oracle (sampled)")
+    assert_close(to_np(state[bs][:, ds]), ref_last, rtol, atol, "decode state vs oracle (sampled)")
+    # forward scan of the same tokens from the same state, all elements
+    tr = lambda t: t.transpose(0, 1).contiguous()
+    fo, fl = ssm_scan_fwd(tr(tok["x"]), tr(tok["delta"]), tok["A"], tr(tok["B"]), tr(tok["C"]),
+                          D=tok["D"], z=tr(tok["z"]), delta_bias=tok["delta_bias"],
+                          initial_state=tok["state0"], return_last_state=True)
+    torch.cuda.synchronize()
+    fgot = fo[bs][..., ds]
+    assert_close(to_np(fgot), ref, rtol, atol, "forward of decode tokens vs oracle (sampled)")
+    for s0 in range(0, steps, 128):
+        assert_close(to_np(outs[s0:s0 + 128]), to_np(fo[:, s0:s0 + 128].transpose(0, 1)),
+                     2 * rtol, 2 * atol, "decode chain vs forward, steps %d.." % s0)
+    assert_close(to_np(state), to_np(fl), 2 * rtol, 2 * atol, "decode final state vs forward")
