@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Selective-scan benchmark on one MI355X.
+
+A step is one ssm_scan_fwd call over one batch of the Mamba-130M-shaped
+layer (batch 4, seq 2048, 1536 channels, N=16, bf16 activations, float32
+state, z gate on): every row of the hot path (softplus, decay, input term,
+recurrence, readout + skip, gate, store) runs in that one launch.  Inputs are
+resident in HBM before timing starts; each step reads a different replica of
+the inputs, and the replicas together are several times the 256 MB MALL, so
+steady-state steps stream from HBM rather than the last-level cache.
+
+Prints ONE JSON line (the metric named on the config) with the roofline of
+the forward kernel and the float64 oracle timed on the host as a baseline,
+plus secondary lines-in-one for the other workloads (2.8B-shaped layer,
+131k-token long context, one decode step).
+
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+                  [--no-secondary]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, vendor peak
+MALL_BYTES = 256 << 20      # Infinity Cache (last-level) capacity
+WORKLOAD = "mamba130m_bf16"
+METRIC = "selective-scan fwd tokens·channels/s + achieved HBM GB/s (% of peak), 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_mamba130m_bf16_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "selective_state_space_31_amd", "csrc", "ssm_scan.hip")
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = enough to exceed 4x MALL)")
+    return ap.parse_args()
+
+
+def time_launches(fn, args_list, warmup, steps, torch):
+    """Run fn(*args_list[i % R]) warmup+steps times; events bracket each timed
+    launch on the stream the kernel runs on (torch's current stream).
+    Returns (total_ms, per-launch ms list)."""
+    stream = torch.cuda.current_stream()
+    R = len(args_list)
+    for i in range(warmup):
+        fn(*args_list[i % R])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(*args_list[(warmup + i) % R])
+        ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in ev]
+
+
+def fwd_case(name, steps, warmup, replicas, torch, ops, W, seed=0):
+    c = dict(W.CONFIGS[name])
+    dev = torch.device("cuda:0")
+    alg = W.algorithmic_bytes(c["batch"], c["L"], c["dim"], c["dstate"], c["dtype"], c["gate"],
+                              c["last_state"])
+    R = replicas or max(1, min(8, -(-4 * MALL_BYTES // alg)))
+    probs = [W.make_problem(**c, seed=seed + r, device=dev, engine="torch_cuda") for r in range(R)]
+    outs = [torch.empty_like(p.x) for p in probs]
+    lasts = [torch.empty(c["batch"], c["dim"], c["dstate"], device=dev) if c["last_state"] else None
+             for _ in probs]
+
+    def call(p, o, l):
+        ops.ssm_scan_fwd(**p.tensors(), out=o, last_state=l)
+
+    total_ms, per = time_launches(call, list(zip(probs, outs, lasts)), warmup, steps, torch)
+    per.sort()
+    ms = total_ms / steps
+    kern_ms = sum(per) / len(per)
+    toks = c["batch"] * c["L"] * c["dim"]
+    res = dict(workload=name, batch=c["batch"], seq_len=c["L"], dim=c["dim"], dstate=c["dstate"],
+               dtype=c["dtype"], gate=c["gate"], last_state=c["last_state"], input_replicas=R,
+               ms_per_step=ms, kernel_ms_avg=kern_ms, kernel_ms_median=per[len(per) // 2],
+               tokens_channels_per_s=toks / (ms * 1e-3), algorithmic_bytes=alg,
+               achieved_GBps=alg / (kern_ms * 1e-3) / 1e9)
+    res["pct_of_hbm_peak"] = 100.0 * res["achieved_GBps"] / HBM_PEAK_GBPS
+    del probs, outs, lasts
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_case(steps, warmup, torch, ops, W):
+    c = W.CONFIGS["decode_fp32"]
+    dev = torch.device("cuda:0")
+    nsl = 16  # distinct token slices cycled through (the state is updated in place every step)
+    tok = W.make_decode_tokens(nsl, c["batch"], c["dim"], c["dstate"], seed=0, device=dev)
+    state = tok["state0"].clone()
+    out = torch.empty(c["batch"], c["dim"], device=dev)
+
+    def call(s):
+        ops.ssm_state_update(state, tok["x"][s], tok["delta"][s], tok["A"], tok["B"][s], tok["C"][s],
+                             D=tok["D"], z=tok["z"][s], delta_bias=tok["delta_bias"], out=out)
+
+    total_ms, per = time_launches(call, [(s,) for s in range(nsl)], warmup, steps, torch)
+    alg = W.decode_step_bytes(c["batch"], c["dim"], c["dstate"])
+    kern_ms = sum(per) / len(per)
+    # 1024 chained steps, wall clock on the stream
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s in range(c["steps"]):
+        call(s % nsl)
+    t1.record()
+    torch.cuda.synchronize()
+    res = dict(workload="decode_fp32", batch=c["batch"], dim=c["dim"], dstate=c["dstate"],
+               ms_per_step=total_ms / steps, kernel_ms_avg=kern_ms,
+               tokens_channels_per_s=c["batch"] * c["dim"] / (kern_ms * 1e-3),
+               algorithmic_bytes=alg, achieved_GBps=alg / (kern_ms * 1e-3) / 1e9,
+               chain_1024_steps_ms=t0.elapsed_time(t1))
+    res["pct_of_hbm_peak"] = 100.0 * res["achieved_GBps"] / HBM_PEAK_GBPS
+    note = ("one step moves %.0f MB, inside the 256 MB MALL: consecutive steps re-read the "
+            "state from cache, so this rate can exceed what HBM alone delivers" % (alg / 1e6))
+    res["note"] = note
+    return res
+
+
+def cpu_baseline(W, torch):
+    """The float64 oracle as it stands, on the host cores, over the same
+    workload: one whole batch of the 130M-shaped layer (all channels, all
+    tokens), from the same generator, bf16 values widened exactly."""
+    import oracle
+    c = dict(W.CONFIGS[WORKLOAD])
+    p = W.make_problem(**c, seed=0, device="cpu", engine="numpy")
+    nthreads = oracle.oracle.default_threads()
+    h = p.host_f32()
+    t = time.perf_counter()
+    oracle.scan(h["x"], h["delta"], h["A"], h["B"], h["C"], D=h["D"], z=h["z"],
+                delta_bias=h["delta_bias"], nthreads=nthreads)
+    dt = time.perf_counter() - t
+    toks = c["batch"] * c["L"] * c["dim"]
+    return dict(value=toks / dt, unit="tokens*channels/s", cores=nthreads, kind="oracle",
+                sample="one full batch: %d x %d tokens x %d channels, N=%d (%.2f s wall on %d threads)"
+                       % (c["batch"], c["L"], c["dim"], c["dstate"], dt, nthreads))
+
+
+def traffic_entry(kernel_ms):
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE,
+    WRITE_SIZE, scaled by a copy-kernel calibration), if they were taken on
+    the kernel source as it is now; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested); run with --gpus 1." % a.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import selective_state_space_31_amd as ops
+    from selective_state_space_31_amd import workloads as W
+    ops.load_library()
+    torch.cuda.init()
+
+    main_res = fwd_case(WORKLOAD, a.steps, a.warmup, a.replicas, torch, ops, W)
+    secondary = {}
+    if not a.no_secondary:
+        secondary["mamba2p8b_bf16"] = fwd_case("mamba2p8b_bf16", max(5, a.steps // 5), 3, 0, torch, ops, W)
+        secondary["longctx_bf16"] = fwd_case("longctx_bf16", max(3, a.steps // 10), 2, 0, torch, ops, W)
+        c = dict(W.CONFIGS[WORKLOAD])
+        dev = torch.device("cuda:0")
+        R = main_res["input_replicas"]
+        probs = [W.make_problem(**c, seed=r, device=dev, engine="torch_cuda", A_kind="general")
+                 for r in range(R)]
+        outs = [torch.empty_like(p.x) for p in probs]
+        tot, per = time_launches(lambda p, o: ops.ssm_scan_fwd(**p.tensors(), out=o),
+                                 list(zip(probs, outs)), 5, max(10, a.steps // 2), torch)
+        kms = sum(per) / len(per)
+        secondary["mamba130m_bf16_general_A"] = dict(
+            workload="mamba130m_bf16 with a non-structured A (every decay is its own exp)",
+            kernel_ms_avg=kms,
+            tokens_channels_per_s=c["batch"] * c["L"] * c["dim"] / (kms * 1e-3),
+            achieved_GBps=main_res["algorithmic_bytes"] / (kms * 1e-3) / 1e9)
+        del probs, outs
+        torch.cuda.empty_cache()
+        secondary["decode_fp32"] = decode_case(max(20, a.steps), 5, torch, ops, W)
+
+    kern_ms = main_res["kernel_ms_avg"]
+    achieved = main_res["algorithmic_bytes"] / (kern_ms * 1e-3) / 1e9
+    roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic_entry(kern_ms),
+                kernel="fwd_seq_kernel<bf16_t,16,EXACT,softplus,gate>",
+                algorithmic_bytes_per_launch=main_res["algorithmic_bytes"],
+                kernel_ms_avg=round(kern_ms, 5))
+    line = {
+        "metric": METRIC,
+        "value": main_res["tokens_channels_per_s"],
+        "unit": "tokens*channels/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "batch": main_res["batch"], "seq_len": main_res["seq_len"],
+                   "dim": main_res["dim"], "dstate": main_res["dstate"], "gate": True,
+                   "A": "s4d_real (A[d,n] = -(n+1))", "input_replicas": main_res["input_replicas"]},
+        "achieved_GBps": round(achieved, 1),
+        "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
+        "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(W, torch)
+    if secondary:
+        line["secondary"] = secondary
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,482 @@
+// kernels.hpp -- device code of the forward scan (templates), shared by the
+// translation units that instantiate it for each activation type and state
+// width.  Host entry points and the remaining kernels are in ssm_scan.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace ssm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ----------------------------------------------------------------------------
+// element access
+// ----------------------------------------------------------------------------
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v.bits) << 16);
+}
+__device__ __forceinline__ void store_act(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_act(bf16_t* p, float v) {
+  // round to nearest even (gfx950 converts natively)
+  __bf16 b = static_cast<__bf16>(v);
+  p->bits = __builtin_bit_cast(uint16_t, b);
+}
+
+// Buffer-resource access to the per-token activation rows.  The descriptor
+// base is wave-uniform (a token row start, kept in SGPRs), the lane's column
+// is a constant VGPR byte offset, and the token within a group is a scalar
+// offset: no per-access vector address arithmetic.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) 32-bit access, gfx9 family
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kRsrcWord3);
+}
+
+template <typename TA>
+struct Io;
+template <>
+struct Io<float> {
+  using raw_t = uint32_t;
+  static constexpr int es = 4;
+  __device__ static raw_t load(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  }
+  __device__ static float f32(raw_t v) { return __uint_as_float(v); }
+  __device__ static void store(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+  }
+};
+template <>
+struct Io<bf16_t> {
+  using raw_t = uint16_t;
+  static constexpr int es = 2;
+  __device__ static raw_t load(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  }
+  __device__ static float f32(raw_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+  __device__ static void store(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
+    __bf16 b = static_cast<__bf16>(v);  // round to nearest even
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, b), r, voff, soff, 0);
+  }
+};
+
+// B_t / C_t rows are read through the constant address space: the address is
+// wave-uniform, so these become scalar loads into SGPRs.
+typedef const __attribute__((address_space(4))) float cfloat_t;
+typedef const __attribute__((address_space(4))) uint32_t cu32_t;
+typedef const __attribute__((address_space(4))) uint16_t cu16_t;
+
+// Row of NT values of B_t or C_t, widened to f32; with EXACT (dstate == NT)
+// whole dwords are read, otherwise elements up to N with zeros after.
+template <int NT, bool EXACT>
+__device__ __forceinline__ void load_row(const float* p, int N, float (&v)[NT]) {
+  cfloat_t* q = (cfloat_t*)p;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) v[n] = (EXACT || n < N) ? q[n] : 0.0f;
+}
+template <int NT, bool EXACT>
+__device__ __forceinline__ void load_row(const bf16_t* p, int N, float (&v)[NT]) {
+  if constexpr (EXACT && (NT % 2 == 0)) {
+    cu32_t* w = (cu32_t*)p;
+#pragma unroll
+    for (int i = 0; i < NT / 2; ++i) {
+      const uint32_t u = w[i];
+      v[2 * i] = __uint_as_float(u << 16);
+      v[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
+    }
+  } else {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      v[n] = (EXACT || n < N) ? __uint_as_float(static_cast<uint32_t>(q[n]) << 16) : 0.0f;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// scalar functions of the step
+// ----------------------------------------------------------------------------
+// softplus(u) = log(1 + e^u) in float32, accurate to a few ulp relative:
+//   u > 15      : u (the dropped log1p(e^-u) < 3.1e-7 is below u's half-ulp)
+//   e^u < 1/16  : log1p(e) by its series to e^5 (relative error < e^5/6)
+//   otherwise   : log2(1 + e) * ln 2 (1 + e >= 1.0625 keeps cancellation small)
+__device__ __forceinline__ float softplus_f32(float u) {
+  const float e = __builtin_amdgcn_exp2f(u * kLog2e);
+  const float lg = __builtin_amdgcn_logf(1.0f + e) * kLn2;
+  const float p =
+      e * __builtin_fmaf(e, __builtin_fmaf(e, __builtin_fmaf(e, __builtin_fmaf(e, 0.2f, -0.25f),
+                                                               0.33333334f),
+                                             -0.5f),
+                         1.0f);
+  const float r = e < 0.0625f ? p : lg;
+  return u > 15.0f ? u : r;
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^-z); e^-z = inf gives 0 * z = -0.
+__device__ __forceinline__ float silu_f32(float z) {
+  const float e = __builtin_amdgcn_exp2f(-z * kLog2e);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// e^x for float32 x, returned as hi + lo with hi = e^x rounded to nearest
+// (error ~0.5 ulp, no bias) and lo the part of e^x that hi drops.
+// The hardware exp2 is within an ulp but rounds low on average (about
+// -0.05 ulp); a decay factor applied a thousand times over a long memory
+// turns that bias into a relative drift of ~3e-6 in the state, so the paths
+// whose float32 results must track a float64 reference over long horizons
+// use this instead.  Method: x = k ln2 + f with |f| <= ln2/2 (Cody-Waite, ln2
+// split in two), e^f = 1 + f q(f) with q the Taylor series of (e^f - 1)/f to
+// f^6 (truncation < 6e-9 relative), result scaled by 2^k.
+constexpr float kLn2Hi = 0.693145751953125f;        // 11 leading bits of ln 2
+constexpr float kLn2Lo = 1.428606765330187e-06f;    // ln 2 - kLn2Hi
+__device__ __forceinline__ float exp_acc(float x, float& lo) {
+  x = __builtin_fmaxf(x, -104.0f);  // e^-104 is below the smallest float32
+  const float k = __builtin_rintf(x * kLog2e);
+  float f = __builtin_fmaf(-k, kLn2Hi, x);
+  f = __builtin_fmaf(-k, kLn2Lo, f);
+  float q = __builtin_fmaf(f, 1.0f / 5040.0f, 1.0f / 720.0f);
+  q = __builtin_fmaf(f, q, 1.0f / 120.0f);
+  q = __builtin_fmaf(f, q, 1.0f / 24.0f);
+  q = __builtin_fmaf(f, q, 1.0f / 6.0f);
+  q = __builtin_fmaf(f, q, 0.5f);
+  q = __builtin_fmaf(f, q, 1.0f);
+  const float hi = __builtin_fmaf(f, q, 1.0f);
+  const float l = __builtin_fmaf(f, q, 1.0f - hi);  // 1 - hi is exact (hi in [0.7, 1.5])
+  const int ki = static_cast<int>(k);
+  lo = __builtin_ldexpf(l, ki);
+  return __builtin_ldexpf(hi, ki);
+}
+
+// h = a*h + b with the result in h's own register.  Written out so the
+// compiler does not pick the accumulate form (whose accumulator is b) and
+// then copy h back every step.
+__device__ __forceinline__ void fma_inplace(float& h, float a, float b) {
+  h = __builtin_fmaf(a, h, b);
+}
+
+// ----------------------------------------------------------------------------
+// forward
+//
+// Time is cut into K chunks of Lc tokens so that every workload offers the
+// chip enough independent lanes (a lane = one channel over one chunk).  The
+// affine maps h -> a*h + b of consecutive tokens compose associatively
+// (a1,b1) then (a2,b2) = (a2*a1, a2*b1 + b2), so a chunk is summarised by
+// its total decay exp(A[n] * sum Delta) and the state it reaches from zero;
+// three launches then finish the scan:
+//   agg   : per chunk 0..K-2, sum Delta and the local end state from h = 0;
+//   carry : per (sequence, channel, state), fold the chunk summaries in
+//           order, leaving the exact state entering every chunk;
+//   scan  : per chunk, the recurrence from its entering state, with the
+//           readout, skip, gate and store fused in.
+// With K = 1 only the scan runs.
+// ----------------------------------------------------------------------------
+template <typename TA>
+struct FwdArgs {
+  const TA* x;
+  const TA* delta;
+  const float* bias;
+  const float* A;
+  const TA* B;
+  const TA* C;
+  const float* Dsk;
+  const TA* z;
+  TA* out;
+  float* last_state;
+  const float* h0;
+  float* ws_S;  // (batch, K-1, dim): sum of Delta over chunk c
+  float* ws_H;  // (batch, K-1, N, dim): chunk c's end state from zero, then (after
+                // the carry pass) the state entering chunk c+1
+  int L;
+  int Lc;
+  int K;
+  int dim;
+  int N;
+};
+
+constexpr int kGroup = 4;  // tokens per group; the next group's loads are in flight
+
+// Per-lane channel constants.
+template <int NT>
+struct Chan {
+  float A2[NT];  // A[d,n] * log2(e)
+  float A0;      // A[d,0]
+  float bias, dsk;
+  int d0;        // first channel of the wave
+  uint32_t voff_ld, voff_st;
+  bool valid;
+  bool pow;      // every lane of the wave has A[d,n] == (n+1) A[d,0]
+};
+
+template <typename TA, int NT, bool EXACT>
+__device__ __forceinline__ Chan<NT> load_chan(const FwdArgs<TA>& a, int d0) {
+  Chan<NT> c;
+  const int lane = threadIdx.x;
+  const int d = d0 + lane;
+  const int N = a.N;
+  c.d0 = d0;
+  c.valid = d < a.dim;
+  const int dl = c.valid ? d : a.dim - 1;  // masked lanes compute on a valid channel
+  bool pow_ok = true;
+  c.A0 = a.A[static_cast<size_t>(dl) * N];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const float an = (EXACT || n < N) ? a.A[static_cast<size_t>(dl) * N + n] : 0.0f;
+    c.A2[n] = an * kLog2e;
+    if (EXACT || n < N) pow_ok = pow_ok && (an == static_cast<float>(n + 1) * c.A0);
+  }
+  c.pow = __all(pow_ok);
+  c.bias = a.bias ? a.bias[dl] : 0.0f;
+  c.dsk = a.Dsk ? a.Dsk[dl] : 0.0f;
+  c.voff_ld = static_cast<uint32_t>(dl - d0) * Io<TA>::es;
+  c.voff_st = static_cast<uint32_t>(lane) * Io<TA>::es;
+  return c;
+}
+
+// One token: discretise, update the N states, read out, gate.  Returns the
+// output value (before rounding to the activation type).  B_t and C_t are read
+// from their (wave-uniform) rows in blocks of up to 16 states.
+//   POW : the channel's A is (n+1)*A[0], decays are powers of r = e^(Delta*A[0]).
+//   ACC : float32 activations; r is formed to ~0.5 ulp as a two-float hi + lo
+//         and every power is taken against both parts, so r's own rounding is
+//         not amplified (n+1)-fold in r^(n+1).  With bf16 activations the
+//         output rounding (2^-9) dwarfs these errors and the single-float
+//         chain on the hardware exp is used.
+//   AGG : summary pass: no readout, the step size is summed into S instead.
+template <typename TA, int NT, bool EXACT, bool SP, bool GATE, bool POW, bool ACC, bool AGG>
+__device__ __forceinline__ float token_step(float (&h)[NT], const Chan<NT>& ch, const TA* Brow,
+                                            const TA* Crow, int N, float xv, float draw, float zv,
+                                            float& S) {
+  constexpr int NB = NT < 16 ? NT : 16;
+  const float raw = draw + ch.bias;
+  const float dt = SP ? softplus_f32(raw) : raw;
+  const float dx = dt * xv;
+  float y = ch.dsk * xv;
+  if constexpr (AGG) S += dt;
+  float rh = 0.0f, rl = 0.0f, p = 0.0f;
+  if constexpr (POW && ACC) {
+    rh = exp_acc(dt * ch.A0, rl);
+    p = rh;
+  } else if constexpr (POW) {
+    rh = __builtin_amdgcn_exp2f(dt * ch.A2[0]);
+    p = rh;
+  }
+#pragma unroll
+  for (int n0 = 0; n0 < NT; n0 += NB) {
+    float Bv[NB], Cv[NB];
+    load_row<NB, EXACT>(Brow + n0, N - n0, Bv);
+    if constexpr (!AGG) load_row<NB, EXACT>(Crow + n0, N - n0, Cv);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int n = n0 + j;
+      float dA;
+      if constexpr (POW) {
+        dA = p;
+        if constexpr (ACC) {
+          if (n + 1 < NT) p = __builtin_fmaf(p, rh, p * rl);
+        } else {
+          p *= rh;
+        }
+      } else {
+        dA = __builtin_amdgcn_exp2f(dt * ch.A2[n]);
+      }
+      fma_inplace(h[n], dA, dx * Bv[j]);
+      if constexpr (!AGG) y = __builtin_fmaf(Cv[j], h[n], y);
+    }
+  }
+  if constexpr (GATE && !AGG) y *= silu_f32(zv);
+  return y;
+}
+
+// Tokens [t_begin, t_begin + len) of sequence b for the wave's 64 channels.
+// AGG: summary pass (S, h); otherwise the output pass.
+template <typename TA, int NT, bool EXACT, bool SP, bool GATE, bool POW, bool AGG>
+__device__ __forceinline__ void run_tokens(const FwdArgs<TA>& a, const Chan<NT>& ch, int b,
+                                           int t_begin, int len, float (&h)[NT], float& S) {
+  using IO = Io<TA>;
+  using raw_t = typename IO::raw_t;
+  constexpr bool Z = GATE && !AGG;
+  const int dim = a.dim, N = a.N;
+  const size_t rowblk = static_cast<size_t>(b) * static_cast<size_t>(a.L) + t_begin;
+  const uint32_t rowbytes = static_cast<uint32_t>(dim) * IO::es;
+  const uint32_t span = kGroup * rowbytes;
+  const TA* B = a.B + rowblk * N;
+  const TA* C = a.C + rowblk * N;
+  const int d0 = ch.d0;
+  const uint32_t voff_ld = ch.voff_ld, voff_st = ch.voff_st;
+
+  // x/delta/z of kGroup tokens starting at t0 (token indices clamped to the
+  // range, so reads past its end repeat the last row and are unused)
+  auto fetch = [&](int t0, raw_t(&xs)[kGroup], raw_t(&ds)[kGroup], raw_t(&zs)[kGroup]) {
+    const int tb = t0 < len ? t0 : len - 1;
+    const size_t base = (rowblk + tb) * dim + d0;
+    const rsrc_t rx = make_rsrc(a.x + base, span), rd = make_rsrc(a.delta + base, span);
+    const rsrc_t rz = make_rsrc(Z ? a.z + base : a.x + base, span);
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      const int t = (tb + u < len) ? tb + u : len - 1;
+      const uint32_t so = static_cast<uint32_t>(t - tb) * rowbytes;
+      xs[u] = IO::load(rx, voff_ld, so);
+      ds[u] = IO::load(rd, voff_ld, so);
+      if constexpr (Z) zs[u] = IO::load(rz, voff_ld, so);
+    }
+  };
+  // kGroup tokens starting at t0, all inside the range
+  auto compute = [&](int t0, const raw_t(&xs)[kGroup], const raw_t(&ds)[kGroup],
+                     const raw_t(&zs)[kGroup]) {
+    const size_t obase = (rowblk + t0) * dim + d0;
+    const rsrc_t ro = make_rsrc(a.out + (AGG ? 0 : obase), span);
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      const size_t row = static_cast<size_t>(t0 + u) * N;
+      const float y = token_step<TA, NT, EXACT, SP, GATE, POW, IO::es == 4, AGG>(
+          h, ch, B + row, C + row, N, IO::f32(xs[u]), IO::f32(ds[u]), Z ? IO::f32(zs[u]) : 0.0f, S);
+      if constexpr (!AGG)
+        if (ch.valid) IO::store(y, ro, voff_st, static_cast<uint32_t>(u) * rowbytes);
+    }
+  };
+
+  // Main part: pairs of full groups, ping-ponging two register buffers so the
+  // loads of the next group are in flight while the current one computes,
+  // and no per-token branch splits the unrolled recurrence.  (Wide states,
+  // N > 16, take the compact token-at-a-time loop below for all tokens.)
+  int t_tail = 0;
+  if constexpr (NT <= 16) {
+    const int npair = len / (2 * kGroup);
+    raw_t xa[kGroup], da[kGroup], za[kGroup], xb2[kGroup], db2[kGroup], zb2[kGroup];
+    fetch(0, xa, da, za);
+    for (int i = 0; i < npair; ++i) {
+      const int t0 = i * 2 * kGroup;
+      fetch(t0 + kGroup, xb2, db2, zb2);
+      compute(t0, xa, da, za);
+      fetch(t0 + 2 * kGroup, xa, da, za);
+      compute(t0 + kGroup, xb2, db2, zb2);
+    }
+    t_tail = npair * 2 * kGroup;
+  }
+  // Tail: the remaining tokens one at a time.
+  for (int t = t_tail; t < len; ++t) {
+    const size_t base = (rowblk + t) * dim + d0;
+    const rsrc_t rx = make_rsrc(a.x + base, rowbytes), rd = make_rsrc(a.delta + base, rowbytes);
+    float zv = 0.0f;
+    if constexpr (Z) zv = IO::f32(IO::load(make_rsrc(a.z + base, rowbytes), voff_ld, 0));
+    const size_t row = static_cast<size_t>(t) * N;
+    const float y = token_step<TA, NT, EXACT, SP, GATE, POW, IO::es == 4, AGG>(
+        h, ch, B + row, C + row, N, IO::f32(IO::load(rx, voff_ld, 0)),
+        IO::f32(IO::load(rd, voff_ld, 0)), zv, S);
+    if constexpr (!AGG)
+      if (ch.valid) IO::store(y, make_rsrc(a.out + base, rowbytes), voff_st, 0);
+  }
+}
+
+// Summary pass: block (channel tile, chunk c < K-1, sequence b).
+template <typename TA, int NT, bool EXACT, bool SP>
+__global__ void __launch_bounds__(64) fwd_agg_kernel(FwdArgs<TA> a) {
+  const int d0 = blockIdx.x * 64;
+  const int c = blockIdx.y;
+  const int b = blockIdx.z;
+  const Chan<NT> ch = load_chan<TA, NT, EXACT>(a, d0);
+  float h[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) h[n] = 0.0f;
+  float S = 0.0f;
+  const int t_begin = c * a.Lc;  // chunks before the last are full
+  if (ch.pow)
+    run_tokens<TA, NT, EXACT, SP, false, true, true>(a, ch, b, t_begin, a.Lc, h, S);
+  else
+    run_tokens<TA, NT, EXACT, SP, false, false, true>(a, ch, b, t_begin, a.Lc, h, S);
+  if (ch.valid) {
+    const int d = d0 + threadIdx.x;
+    const size_t slot = static_cast<size_t>(b) * (a.K - 1) + c;
+    a.ws_S[slot * a.dim + d] = S;
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      if (EXACT || n < a.N) a.ws_H[(slot * a.N + n) * a.dim + d] = h[n];
+  }
+}
+
+// Output pass: block (channel tile, chunk c, sequence b).
+template <typename TA, int NT, bool EXACT, bool SP, bool GATE>
+__global__ void __launch_bounds__(64) fwd_scan_kernel(FwdArgs<TA> a) {
+  const int d0 = blockIdx.x * 64;
+  const int c = blockIdx.y;
+  const int b = blockIdx.z;
+  const Chan<NT> ch = load_chan<TA, NT, EXACT>(a, d0);
+  const int N = a.N;
+  const int d = d0 + threadIdx.x;
+  const int dl = ch.valid ? d : a.dim - 1;
+  float h[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) h[n] = 0.0f;
+  if (c == 0) {
+    if (a.h0) {
+      const float* hp = a.h0 + (static_cast<size_t>(b) * a.dim + dl) * N;
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        if (EXACT || n < N) h[n] = hp[n];
+    }
+  } else {
+    const size_t slot = static_cast<size_t>(b) * (a.K - 1) + (c - 1);
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      if (EXACT || n < N) h[n] = a.ws_H[(slot * N + n) * a.dim + dl];
+  }
+  const int t_begin = c * a.Lc;
+  const int len = (a.L - t_begin < a.Lc) ? a.L - t_begin : a.Lc;
+  float S = 0.0f;
+  if (len > 0) {  // an empty sequence only carries the initial state through
+    if (ch.pow)
+      run_tokens<TA, NT, EXACT, SP, GATE, true, false>(a, ch, b, t_begin, len, h, S);
+    else
+      run_tokens<TA, NT, EXACT, SP, GATE, false, false>(a, ch, b, t_begin, len, h, S);
+  }
+  if (a.last_state && ch.valid && c == a.K - 1) {
+    float* lp = a.last_state + (static_cast<size_t>(b) * a.dim + d) * N;
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      if (EXACT || n < N) lp[n] = h[n];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// launchers (host side of the templates above)
+// ----------------------------------------------------------------------------
+int launch_status(const char* what);
+void launch_carry(const float* A, const float* h0, const float* ws_S, float* ws_H, int64_t batch,
+                  int dim, int N, int K, hipStream_t s);
+
+template <typename TA, int NT, bool EXACT, bool SP, bool GATE>
+int launch_fwd(const FwdArgs<TA>& a, int64_t batch, hipStream_t s) {
+  const unsigned tiles = static_cast<unsigned>((a.dim + 63) / 64);
+  if (a.K > 1) {
+    hipLaunchKernelGGL((fwd_agg_kernel<TA, NT, EXACT, SP>),
+                       dim3(tiles, static_cast<unsigned>(a.K - 1), static_cast<unsigned>(batch)),
+                       dim3(64), 0, s, a);
+    launch_carry(a.A, a.h0, a.ws_S, a.ws_H, batch, a.dim, a.N, a.K, s);
+  }
+  hipLaunchKernelGGL((fwd_scan_kernel<TA, NT, EXACT, SP, GATE>),
+                     dim3(tiles, static_cast<unsigned>(a.K), static_cast<unsigned>(batch)),
+                     dim3(64), 0, s, a);
+  return launch_status("ssm_scan_fwd");
+}
+
+template <typename TA, int NT, bool EXACT>
+int launch_fwd_flags(const FwdArgs<TA>& a, int64_t batch, bool sp, bool gate, hipStream_t s) {
+  if (sp)
+    return gate ? launch_fwd<TA, NT, EXACT, true, true>(a, batch, s)
+                : launch_fwd<TA, NT, EXACT, true, false>(a, batch, s);
+  return gate ? launch_fwd<TA, NT, EXACT, false, true>(a, batch, s)
+              : launch_fwd<TA, NT, EXACT, false, false>(a, batch, s);
+}
+
+
+}  // namespace ssm
