@@ -28,16 +28,29 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, vendor peak
+# non-packed fp32 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz
+VALU_PEAK_TFLOPS = 78.6
+# algorithmic work of the scan: per state element the decay (multiply + exp,
+# counted 1), the input term (multiply) and two FMAs (2 each); per token and
+# channel softplus, skip and gate (counted 10)
+FLOPS_PER_STATE_ELEMENT = 7
+FLOPS_PER_TOKEN_CHANNEL = 10
 MALL_BYTES = 256 << 20      # Infinity Cache (last-level) capacity
 WORKLOAD = "mamba130m_bf16"
 METRIC = "selective-scan fwd tokens·channels/s + achieved HBM GB/s (% of peak), 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_mamba130m_bf16_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "selective_state_space_31_amd", "csrc", "ssm_scan.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "selective_state_space_31_amd", "csrc", f)
+               for f in ("kernels.hpp", "ssm_scan.hip")]
 
 
 def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the forward kernels' sources, recorded with traffic counters so
+    that counters taken on other code are never reported."""
+    h = hashlib.sha256()
+    for p in KERNEL_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -48,6 +61,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = enough to exceed 4x MALL)")
+    ap.add_argument("--only", default=None,
+                    help="time just this forward workload (for profiling runs); prints its record")
     return ap.parse_args()
 
 
@@ -104,37 +119,40 @@ def fwd_case(name, steps, warmup, replicas, torch, ops, W, seed=0):
 
 
 def decode_case(steps, warmup, torch, ops, W):
+    """One decode step of 256 sequences x 5120 channels x N=16 (float32 state,
+    updated in place).  Steps rotate over several layers' states and token
+    slices, as a decoder stepping through a model would, so the working set
+    (~1 GB) exceeds the MALL and the state streams from HBM."""
     c = W.CONFIGS["decode_fp32"]
     dev = torch.device("cuda:0")
-    nsl = 16  # distinct token slices cycled through (the state is updated in place every step)
+    nsl, nlayer = 16, 4
     tok = W.make_decode_tokens(nsl, c["batch"], c["dim"], c["dstate"], seed=0, device=dev)
-    state = tok["state0"].clone()
+    states = [tok["state0"].clone() for _ in range(nlayer)]
     out = torch.empty(c["batch"], c["dim"], device=dev)
 
-    def call(s):
-        ops.ssm_state_update(state, tok["x"][s], tok["delta"][s], tok["A"], tok["B"][s], tok["C"][s],
-                             D=tok["D"], z=tok["z"][s], delta_bias=tok["delta_bias"], out=out)
+    def call(s, layer):
+        ops.ssm_state_update(states[layer], tok["x"][s], tok["delta"][s], tok["A"], tok["B"][s],
+                             tok["C"][s], D=tok["D"], z=tok["z"][s], delta_bias=tok["delta_bias"],
+                             out=out)
 
-    total_ms, per = time_launches(call, [(s,) for s in range(nsl)], warmup, steps, torch)
+    args = [(i % nsl, i % nlayer) for i in range(nsl * nlayer)]
+    total_ms, per = time_launches(call, args, warmup, steps, torch)
     alg = W.decode_step_bytes(c["batch"], c["dim"], c["dstate"])
     kern_ms = sum(per) / len(per)
-    # 1024 chained steps, wall clock on the stream
+    # the workload as stated: 1024 chained steps of one layer, wall clock on the stream
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for s in range(c["steps"]):
-        call(s % nsl)
+        call(s % nsl, 0)
     t1.record()
     torch.cuda.synchronize()
     res = dict(workload="decode_fp32", batch=c["batch"], dim=c["dim"], dstate=c["dstate"],
-               ms_per_step=total_ms / steps, kernel_ms_avg=kern_ms,
+               layers_rotated=nlayer, ms_per_step=total_ms / steps, kernel_ms_avg=kern_ms,
                tokens_channels_per_s=c["batch"] * c["dim"] / (kern_ms * 1e-3),
                algorithmic_bytes=alg, achieved_GBps=alg / (kern_ms * 1e-3) / 1e9,
                chain_1024_steps_ms=t0.elapsed_time(t1))
     res["pct_of_hbm_peak"] = 100.0 * res["achieved_GBps"] / HBM_PEAK_GBPS
-    note = ("one step moves %.0f MB, inside the 256 MB MALL: consecutive steps re-read the "
-            "state from cache, so this rate can exceed what HBM alone delivers" % (alg / 1e6))
-    res["note"] = note
     return res
 
 
@@ -183,6 +201,30 @@ def main():
     ops.load_library()
     torch.cuda.init()
 
+    if a.only:
+        if a.only == "microbench":
+            # vector-ALU and HBM stream rates (the built rate microbenchmark)
+            import subprocess
+            exe = os.path.join(ROOT, "selective_state_space_31_amd", "ssm_rates_microbench")
+            r = subprocess.run([exe], stdout=subprocess.PIPE, text=True)
+            print(r.stdout, end="")
+            sys.exit(r.returncode)
+        if a.only == "copy_calibration":
+            # a plain 1 GiB device-to-device copy: the known-size reference for
+            # scaling the FETCH_SIZE / WRITE_SIZE counters to bytes
+            n = 1 << 28
+            src = torch.ones(n, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(a.steps):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            print(json.dumps({"copy_bytes_each_way": n * 4, "copies": a.steps}))
+            return
+        if a.only == "decode_fp32":
+            print(json.dumps(decode_case(a.steps, a.warmup, torch, ops, W)))
+        else:
+            print(json.dumps(fwd_case(a.only, a.steps, a.warmup, a.replicas, torch, ops, W)))
+        return
     main_res = fwd_case(WORKLOAD, a.steps, a.warmup, a.replicas, torch, ops, W)
     secondary = {}
     if not a.no_secondary:
@@ -208,10 +250,16 @@ def main():
 
     kern_ms = main_res["kernel_ms_avg"]
     achieved = main_res["algorithmic_bytes"] / (kern_ms * 1e-3) / 1e9
-    roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic_entry(kern_ms),
-                kernel="fwd_seq_kernel<bf16_t,16,EXACT,softplus,gate>",
+    c = W.CONFIGS[WORKLOAD]
+    elems = c["batch"] * c["L"] * c["dim"] * c["dstate"]
+    flops = FLOPS_PER_STATE_ELEMENT * elems + FLOPS_PER_TOKEN_CHANNEL * c["batch"] * c["L"] * c["dim"]
+    tflops = flops / (kern_ms * 1e-3) / 1e12
+    roof = dict(bound="alu", achieved=round(tflops, 2), peak=VALU_PEAK_TFLOPS, unit="TFLOP/s",
+                frac=round(tflops / VALU_PEAK_TFLOPS, 4), traffic=traffic_entry(kern_ms),
+                kernel="ssm_scan_fwd call = fwd_agg_kernel + fwd_carry_kernel + fwd_scan_kernel",
+                algorithmic_flops_per_launch=flops,
                 algorithmic_bytes_per_launch=main_res["algorithmic_bytes"],
+                hbm_GBps=round(achieved, 1), hbm_frac_of_peak=round(achieved / HBM_PEAK_GBPS, 4),
                 kernel_ms_avg=round(kern_ms, 5))
     line = {
         "metric": METRIC,

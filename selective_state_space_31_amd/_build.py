@@ -25,6 +25,10 @@ FLAGS = [
 ]
 
 
+MICRO_SRC = os.path.join(CSRC, "microbench", "rates.hip")
+MICRO_EXE = os.path.join(PKG, "ssm_rates_microbench")
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
@@ -53,6 +57,11 @@ def build(verbose=False, jobs=None):
             if o.strip():
                 print(o)
     os.replace(tmp, LIB)
+    # the rate microbenchmark behind the roofline figures (a separate executable)
+    tmp = MICRO_EXE + ".tmp%d" % os.getpid()
+    _run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+          "-Xclang", "-packed-fp32-ops", "-o", tmp, MICRO_SRC])
+    os.replace(tmp, MICRO_EXE)
     return LIB
 
 

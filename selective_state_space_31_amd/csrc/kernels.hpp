@@ -204,6 +204,7 @@ struct FwdArgs {
 };
 
 constexpr int kGroup = 4;  // tokens per group; the next group's loads are in flight
+constexpr uint32_t kOutOfRange = 0x80000000u;  // > any descriptor's byte range (those are < 2^31)
 
 // Per-lane channel constants.
 template <int NT>
@@ -238,13 +239,15 @@ __device__ __forceinline__ Chan<NT> load_chan(const FwdArgs<TA>& a, int d0) {
   c.bias = a.bias ? a.bias[dl] : 0.0f;
   c.dsk = a.Dsk ? a.Dsk[dl] : 0.0f;
   c.voff_ld = static_cast<uint32_t>(dl - d0) * Io<TA>::es;
-  c.voff_st = static_cast<uint32_t>(lane) * Io<TA>::es;
+  // Lanes past the last channel store to an offset beyond every descriptor's
+  // range: raw buffer stores out of range are dropped by the hardware, so the
+  // store needs no branch (which would split the unrolled token group).
+  c.voff_st = c.valid ? static_cast<uint32_t>(lane) * Io<TA>::es : kOutOfRange;
   return c;
 }
 
 // One token: discretise, update the N states, read out, gate.  Returns the
-// output value (before rounding to the activation type).  B_t and C_t are read
-// from their (wave-uniform) rows in blocks of up to 16 states.
+// output value (before rounding to the activation type).
 //   POW : the channel's A is (n+1)*A[0], decays are powers of r = e^(Delta*A[0]).
 //   ACC : float32 activations; r is formed to ~0.5 ulp as a two-float hi + lo
 //         and every power is taken against both parts, so r's own rounding is
@@ -252,49 +255,110 @@ __device__ __forceinline__ Chan<NT> load_chan(const FwdArgs<TA>& a, int d0) {
 //         output rounding (2^-9) dwarfs these errors and the single-float
 //         chain on the hardware exp is used.
 //   AGG : summary pass: no readout, the step size is summed into S instead.
+// The step is split in three so that the B_t/C_t rows can be supplied either
+// whole (already in SGPRs) or in blocks of 16 states (wide states).
+struct StepScalars {
+  float dt, dx, y, rh, rl, p;
+};
+
+template <int NT, bool SP, bool POW, bool ACC, bool AGG>
+__device__ __forceinline__ StepScalars step_begin(const Chan<NT>& ch, float xv, float draw,
+                                                  float& S) {
+  StepScalars s;
+  const float raw = draw + ch.bias;
+  s.dt = SP ? softplus_f32(raw) : raw;
+  s.dx = s.dt * xv;
+  s.y = ch.dsk * xv;
+  if constexpr (AGG) S += s.dt;
+  s.rh = s.rl = s.p = 0.0f;
+  if constexpr (POW && ACC) {
+    s.rh = exp_acc(s.dt * ch.A0, s.rl);
+    s.p = s.rh;
+  } else if constexpr (POW) {
+    s.rh = __builtin_amdgcn_exp2f(s.dt * ch.A2[0]);
+    s.p = s.rh;
+  }
+  return s;
+}
+
+// States n0 .. n0+NB-1 given their B_t and C_t values.
+template <int NT, int NB, bool POW, bool ACC, bool AGG>
+__device__ __forceinline__ void step_block(float (&h)[NT], const Chan<NT>& ch, StepScalars& s,
+                                           int n0, const float (&Bv)[NB], const float (&Cv)[NB]) {
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int n = n0 + j;
+    float dA;
+    if constexpr (POW) {
+      dA = s.p;
+      if constexpr (ACC) {
+        if (n + 1 < NT) s.p = __builtin_fmaf(s.p, s.rh, s.p * s.rl);
+      } else {
+        s.p *= s.rh;
+      }
+    } else {
+      dA = __builtin_amdgcn_exp2f(s.dt * ch.A2[n]);
+    }
+    fma_inplace(h[n], dA, s.dx * Bv[j]);
+    if constexpr (!AGG) s.y = __builtin_fmaf(Cv[j], h[n], s.y);
+  }
+}
+
+template <bool GATE, bool AGG>
+__device__ __forceinline__ float step_end(const StepScalars& s, float zv) {
+  float y = s.y;
+  if constexpr (GATE && !AGG) y *= silu_f32(zv);
+  return y;
+}
+
+// Wide or padded states: rows read in blocks of up to 16 inside the step.
 template <typename TA, int NT, bool EXACT, bool SP, bool GATE, bool POW, bool ACC, bool AGG>
 __device__ __forceinline__ float token_step(float (&h)[NT], const Chan<NT>& ch, const TA* Brow,
                                             const TA* Crow, int N, float xv, float draw, float zv,
                                             float& S) {
   constexpr int NB = NT < 16 ? NT : 16;
-  const float raw = draw + ch.bias;
-  const float dt = SP ? softplus_f32(raw) : raw;
-  const float dx = dt * xv;
-  float y = ch.dsk * xv;
-  if constexpr (AGG) S += dt;
-  float rh = 0.0f, rl = 0.0f, p = 0.0f;
-  if constexpr (POW && ACC) {
-    rh = exp_acc(dt * ch.A0, rl);
-    p = rh;
-  } else if constexpr (POW) {
-    rh = __builtin_amdgcn_exp2f(dt * ch.A2[0]);
-    p = rh;
-  }
+  StepScalars s = step_begin<NT, SP, POW, ACC, AGG>(ch, xv, draw, S);
 #pragma unroll
   for (int n0 = 0; n0 < NT; n0 += NB) {
     float Bv[NB], Cv[NB];
     load_row<NB, EXACT>(Brow + n0, N - n0, Bv);
     if constexpr (!AGG) load_row<NB, EXACT>(Crow + n0, N - n0, Cv);
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int n = n0 + j;
-      float dA;
-      if constexpr (POW) {
-        dA = p;
-        if constexpr (ACC) {
-          if (n + 1 < NT) p = __builtin_fmaf(p, rh, p * rl);
-        } else {
-          p *= rh;
-        }
-      } else {
-        dA = __builtin_amdgcn_exp2f(dt * ch.A2[n]);
-      }
-      fma_inplace(h[n], dA, dx * Bv[j]);
-      if constexpr (!AGG) y = __builtin_fmaf(Cv[j], h[n], y);
-    }
+    step_block<NT, NB, POW, ACC, AGG>(h, ch, s, n0, Bv, Cv);
   }
-  if constexpr (GATE && !AGG) y *= silu_f32(zv);
-  return y;
+  return step_end<GATE, AGG>(s, zv);
+}
+
+// Raw words of one token's B and C rows (whole rows of NT <= 16 states),
+// loaded by scalar loads one token ahead of their use.
+template <typename TA, int NT>
+struct RowsRaw {
+  static constexpr int W = static_cast<int>(sizeof(TA)) * NT / 4;  // dwords per row
+  uint32_t b[W], c[W];
+};
+
+template <typename TA, int NT, bool AGG>
+__device__ __forceinline__ void rows_load(RowsRaw<TA, NT>& r, const TA* Brow, const TA* Crow) {
+  cu32_t* qb = (cu32_t*)Brow;
+  cu32_t* qc = (cu32_t*)Crow;
+#pragma unroll
+  for (int i = 0; i < RowsRaw<TA, NT>::W; ++i) {
+    r.b[i] = qb[i];
+    if constexpr (!AGG) r.c[i] = qc[i];
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void rows_unpack(const uint32_t* w, float (&v)[NT], float) {
+#pragma unroll
+  for (int n = 0; n < NT; ++n) v[n] = __uint_as_float(w[n]);
+}
+template <int NT>
+__device__ __forceinline__ void rows_unpack(const uint32_t* w, float (&v)[NT], bf16_t) {
+#pragma unroll
+  for (int i = 0; i < NT / 2; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
 }
 
 // Tokens [t_begin, t_begin + len) of sequence b for the wave's 64 channels.
@@ -330,6 +394,31 @@ __device__ __forceinline__ void run_tokens(const FwdArgs<TA>& a, const Chan<NT>&
       if constexpr (Z) zs[u] = IO::load(rz, voff_ld, so);
     }
   };
+  // Rows of B_t/C_t run one token ahead in SGPRs (whole-row state widths):
+  // the wait for token t's rows is followed by the loads for token t+1, and
+  // scheduling barriers keep the compiler from hoisting a whole group's loads
+  // (which would overflow the scalar registers into vector lanes).
+  constexpr bool PF = EXACT && NT <= 16 && (sizeof(TA) * NT) % 4 == 0;
+  RowsRaw<TA, NT> nxt;
+  if constexpr (PF) rows_load<TA, NT, AGG>(nxt, B, C);
+  auto one = [&](int t, float xv, float draw, float zv) -> float {
+    if constexpr (PF) {
+      float Bv[NT], Cv[NT];
+      rows_unpack<NT>(nxt.b, Bv, TA{});
+      if constexpr (!AGG) rows_unpack<NT>(nxt.c, Cv, TA{});
+      __builtin_amdgcn_sched_barrier(0);
+      const size_t rn = static_cast<size_t>(t + 1 < len ? t + 1 : len - 1) * N;
+      rows_load<TA, NT, AGG>(nxt, B + rn, C + rn);
+      __builtin_amdgcn_sched_barrier(0);
+      StepScalars st = step_begin<NT, SP, POW, IO::es == 4, AGG>(ch, xv, draw, S);
+      step_block<NT, NT, POW, IO::es == 4, AGG>(h, ch, st, 0, Bv, Cv);
+      return step_end<GATE, AGG>(st, zv);
+    } else {
+      const size_t row = static_cast<size_t>(t) * N;
+      return token_step<TA, NT, EXACT, SP, GATE, POW, IO::es == 4, AGG>(h, ch, B + row, C + row, N,
+                                                                       xv, draw, zv, S);
+    }
+  };
   // kGroup tokens starting at t0, all inside the range
   auto compute = [&](int t0, const raw_t(&xs)[kGroup], const raw_t(&ds)[kGroup],
                      const raw_t(&zs)[kGroup]) {
@@ -337,11 +426,8 @@ __device__ __forceinline__ void run_tokens(const FwdArgs<TA>& a, const Chan<NT>&
     const rsrc_t ro = make_rsrc(a.out + (AGG ? 0 : obase), span);
 #pragma unroll
     for (int u = 0; u < kGroup; ++u) {
-      const size_t row = static_cast<size_t>(t0 + u) * N;
-      const float y = token_step<TA, NT, EXACT, SP, GATE, POW, IO::es == 4, AGG>(
-          h, ch, B + row, C + row, N, IO::f32(xs[u]), IO::f32(ds[u]), Z ? IO::f32(zs[u]) : 0.0f, S);
-      if constexpr (!AGG)
-        if (ch.valid) IO::store(y, ro, voff_st, static_cast<uint32_t>(u) * rowbytes);
+      const float y = one(t0 + u, IO::f32(xs[u]), IO::f32(ds[u]), Z ? IO::f32(zs[u]) : 0.0f);
+      if constexpr (!AGG) IO::store(y, ro, voff_st, static_cast<uint32_t>(u) * rowbytes);
     }
   };
 
@@ -369,12 +455,74 @@ __device__ __forceinline__ void run_tokens(const FwdArgs<TA>& a, const Chan<NT>&
     const rsrc_t rx = make_rsrc(a.x + base, rowbytes), rd = make_rsrc(a.delta + base, rowbytes);
     float zv = 0.0f;
     if constexpr (Z) zv = IO::f32(IO::load(make_rsrc(a.z + base, rowbytes), voff_ld, 0));
-    const size_t row = static_cast<size_t>(t) * N;
-    const float y = token_step<TA, NT, EXACT, SP, GATE, POW, IO::es == 4, AGG>(
-        h, ch, B + row, C + row, N, IO::f32(IO::load(rx, voff_ld, 0)),
-        IO::f32(IO::load(rd, voff_ld, 0)), zv, S);
-    if constexpr (!AGG)
-      if (ch.valid) IO::store(y, make_rsrc(a.out + base, rowbytes), voff_st, 0);
+    const float y = one(t, IO::f32(IO::load(rx, voff_ld, 0)), IO::f32(IO::load(rd, voff_ld, 0)), zv);
+    if constexpr (!AGG) IO::store(y, make_rsrc(a.out + base, rowbytes), voff_st, 0);
+  }
+}
+
+// Summary of a full chunk by reverse accumulation (power-structured A,
+// single-float chain): the state the chunk reaches from zero is
+//   H[n] = sum_t (prod_{s>t} r_s)^(n+1) * dx_t * B_t[n],
+// so walking the tokens from last to first with Q = prod_{s>t} r_s, the weight
+// w_n = dx_t * Q^(n+1) follows the chain w_n = w_(n-1) * Q and each state costs
+// one multiply plus one FMA whose addend operand B_t[n] is a scalar register
+// (the forward recurrence needs a third operation, dx * B, per state).
+template <typename TA, int NT, bool SP>
+__device__ __forceinline__ void agg_reverse(const FwdArgs<TA>& a, const Chan<NT>& ch, int b,
+                                            int t_begin, int len, float (&H)[NT], float& S) {
+  using IO = Io<TA>;
+  using raw_t = typename IO::raw_t;
+  const int dim = a.dim, N = a.N;
+  const size_t rowblk = static_cast<size_t>(b) * static_cast<size_t>(a.L) + t_begin;
+  const uint32_t rowbytes = static_cast<uint32_t>(dim) * IO::es;
+  const uint32_t span = kGroup * rowbytes;
+  const TA* B = a.B + rowblk * N;
+  const uint32_t voff_ld = ch.voff_ld;
+  float Q = 1.0f;
+  // x/delta of the kGroup tokens starting at t0 (t0 >= 0, all inside the chunk)
+  auto fetch = [&](int t0, raw_t(&xs)[kGroup], raw_t(&ds)[kGroup]) {
+    const size_t base = (rowblk + t0) * dim + ch.d0;
+    const rsrc_t rx = make_rsrc(a.x + base, span), rd = make_rsrc(a.delta + base, span);
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      xs[u] = IO::load(rx, voff_ld, static_cast<uint32_t>(u) * rowbytes);
+      ds[u] = IO::load(rd, voff_ld, static_cast<uint32_t>(u) * rowbytes);
+    }
+  };
+  RowsRaw<TA, NT> nxt;
+  rows_load<TA, NT, true>(nxt, B + static_cast<size_t>(len - 1) * N, B);
+  auto one = [&](int t, float xv, float draw) {
+    float Bv[NT];
+    rows_unpack<NT>(nxt.b, Bv, TA{});
+    __builtin_amdgcn_sched_barrier(0);
+    const size_t rn = static_cast<size_t>(t > 0 ? t - 1 : 0) * N;
+    rows_load<TA, NT, true>(nxt, B + rn, B);
+    __builtin_amdgcn_sched_barrier(0);
+    const float raw = draw + ch.bias;
+    const float dt = SP ? softplus_f32(raw) : raw;
+    S += dt;
+    const float r = __builtin_amdgcn_exp2f(dt * ch.A2[0]);
+    float w = dt * xv * Q;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      H[n] = __builtin_fmaf(w, Bv[n], H[n]);
+      w *= Q;
+    }
+    Q *= r;
+  };
+  // len is a multiple of 2*kGroup: walk pairs of groups from the end,
+  // ping-ponging two register buffers
+  raw_t xa[kGroup], da[kGroup], xb2[kGroup], db2[kGroup];
+  const int npair = len / (2 * kGroup);
+  fetch(len - kGroup, xa, da);
+  for (int i = npair - 1; i >= 0; --i) {
+    const int t0 = i * 2 * kGroup;  // this pair covers [t0, t0 + 2 kGroup)
+    fetch(t0, xb2, db2);
+#pragma unroll
+    for (int u = kGroup - 1; u >= 0; --u) one(t0 + kGroup + u, IO::f32(xa[u]), IO::f32(da[u]));
+    fetch(t0 >= 2 * kGroup ? t0 - kGroup : t0, xa, da);
+#pragma unroll
+    for (int u = kGroup - 1; u >= 0; --u) one(t0 + u, IO::f32(xb2[u]), IO::f32(db2[u]));
   }
 }
 
@@ -389,10 +537,14 @@ __global__ void __launch_bounds__(64) fwd_agg_kernel(FwdArgs<TA> a) {
 #pragma unroll
   for (int n = 0; n < NT; ++n) h[n] = 0.0f;
   float S = 0.0f;
-  const int t_begin = c * a.Lc;  // chunks before the last are full
-  if (ch.pow)
-    run_tokens<TA, NT, EXACT, SP, false, true, true>(a, ch, b, t_begin, a.Lc, h, S);
-  else
+  const int t_begin = c * a.Lc;  // chunks before the last are full (Lc is a multiple of 2*kGroup)
+  constexpr bool REV = EXACT && NT <= 16 && sizeof(TA) == 2 && (sizeof(TA) * NT) % 4 == 0;
+  if (ch.pow) {
+    if constexpr (REV)
+      agg_reverse<TA, NT, SP>(a, ch, b, t_begin, a.Lc, h, S);
+    else
+      run_tokens<TA, NT, EXACT, SP, false, true, true>(a, ch, b, t_begin, a.Lc, h, S);
+  } else
     run_tokens<TA, NT, EXACT, SP, false, false, true>(a, ch, b, t_begin, a.Lc, h, S);
   if (ch.valid) {
     const int d = d0 + threadIdx.x;

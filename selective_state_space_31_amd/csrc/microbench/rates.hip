@@ -1,0 +1,163 @@
+// rates.hip -- gfx950 rate microbenchmarks behind the roofline figures:
+// vector fp32 FMA / MUL and v_exp_f32 issue rates at several occupancies,
+// and HBM streaming rates (copy, read, in-place update) on buffers larger
+// than the MALL.  Standalone executable; prints one line per measurement.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+
+#define CK(x)                                                                          \
+  do {                                                                                 \
+    hipError_t e_ = (x);                                                               \
+    if (e_ != hipSuccess) {                                                            \
+      std::printf("HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__);      \
+      std::exit(1);                                                                    \
+    }                                                                                  \
+  } while (0)
+
+template <int CH>
+__global__ void __launch_bounds__(256) k_fma(float* out, int iters, float a, float b) {
+  float v[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) v[i] = 1e-3f * (i + threadIdx.x);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) v[i] = __builtin_fmaf(v[i], a, b);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) s += v[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+template <int CH>
+__global__ void __launch_bounds__(256) k_mul(float* out, int iters, float a, float) {
+  float v[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) v[i] = 1e-3f * (i + threadIdx.x);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) v[i] = v[i] * a;
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) s += v[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+template <int CH>
+__global__ void __launch_bounds__(256) k_exp(float* out, int iters, float, float) {
+  float v[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) v[i] = 1e-3f * (i + threadIdx.x);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) v[i] = __builtin_amdgcn_exp2f(-v[i]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) s += v[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ void __launch_bounds__(256) k_copy(const float4* __restrict__ in, float4* __restrict__ out,
+                                              size_t n) {
+  const size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
+  if (i < n) out[i] = in[i];
+}
+
+__global__ void __launch_bounds__(256) k_read(const float4* __restrict__ in, float* __restrict__ out,
+                                              size_t n) {
+  const size_t T = static_cast<size_t>(gridDim.x) * blockDim.x;
+  float s = 0.f;
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n; i += T) {
+    const float4 v = in[i];
+    s += v.x + v.y + v.z + v.w;
+  }
+  if (s == 1234.5f) out[0] = s;  // keeps the loads
+}
+
+__global__ void __launch_bounds__(256) k_inplace(float4* __restrict__ io, size_t n) {
+  const size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
+  if (i < n) {
+    float4 v = io[i];
+    v.x = v.x * 1.0001f + 1.f;
+    v.y *= 0.999f;
+    v.z += 1.f;
+    v.w -= 1.f;
+    io[i] = v;
+  }
+}
+
+int main() {
+  hipDeviceProp_t p;
+  CK(hipGetDeviceProperties(&p, 0));
+  const int cus = p.multiProcessorCount;
+  std::printf("device %s, %d CUs, clock %d kHz\n", p.gcnArchName, cus, p.clockRate);
+  float* out;
+  CK(hipMalloc(&out, static_cast<size_t>(cus) * 16 * 256 * sizeof(float)));
+  hipEvent_t e0, e1;
+  CK(hipEventCreate(&e0));
+  CK(hipEventCreate(&e1));
+  auto timed = [&](auto launch) {
+    launch();
+    CK(hipDeviceSynchronize());
+    float best = 1e30f;
+    for (int r = 0; r < 5; ++r) {
+      CK(hipEventRecord(e0));
+      launch();
+      CK(hipEventRecord(e1));
+      CK(hipEventSynchronize(e1));
+      float ms;
+      CK(hipEventElapsedTime(&ms, e0, e1));
+      if (ms < best) best = ms;
+    }
+    return best;
+  };
+  // --- vector ALU rates: 32 independent chains per lane
+  auto valu = [&](const char* name, void (*k)(float*, int, float, float), int waves_per_simd) {
+    const int iters = 2048, chains = 32;
+    const int blocks = cus * waves_per_simd;  // 256 threads = one wave per SIMD
+    const float ms = timed([&] {
+      hipLaunchKernelGGL(k, dim3(blocks), dim3(256), 0, 0, out, iters, 0.999f, 1e-4f);
+    });
+    const double ops = static_cast<double>(blocks) * 256 * iters * chains;
+    const double rate = ops / (ms * 1e-3);
+    const double lanes_per_clk = rate / (cus * 4.0) / 2.4e9;
+    std::printf("valu %-4s waves/SIMD=%d  %.3e lane-ops/s  %.2f lanes/clk/SIMD  %.2f clk per wave64 op\n",
+                name, waves_per_simd, rate, lanes_per_clk, 64.0 / lanes_per_clk);
+  };
+  for (int w : {1, 2, 4, 8}) valu("fma", k_fma<32>, w);
+  valu("mul", k_mul<32>, 8);
+  valu("exp", k_exp<32>, 8);
+  // --- HBM streams on 2 GiB buffers (8x the MALL)
+  const size_t bytes = static_cast<size_t>(2) << 30, n = bytes / 16;
+  float4 *a, *b;
+  CK(hipMalloc(&a, bytes));
+  CK(hipMalloc(&b, bytes));
+  CK(hipMemset(a, 1, bytes));
+  CK(hipMemset(b, 0, bytes));
+  auto hbm = [&](const char* name, double moved, auto launch) {
+    const float ms = timed(launch);
+    std::printf("hbm  %-40s %8.3f ms  %7.1f GB/s\n", name, ms, moved / (ms * 1e-3) / 1e9);
+  };
+  hbm("copy 2 GiB (read+write)", 2.0 * bytes, [&] {
+    hipLaunchKernelGGL(k_copy, dim3((n + 255) / 256), dim3(256), 0, 0, a, b, n);
+  });
+  hbm("read 2 GiB", 1.0 * bytes, [&] {
+    hipLaunchKernelGGL(k_read, dim3(cus * 16), dim3(256), 0, 0, a, out, n);
+  });
+  hbm("in-place 2 GiB (read+write)", 2.0 * bytes, [&] {
+    hipLaunchKernelGGL(k_inplace, dim3((n + 255) / 256), dim3(256), 0, 0, a, n);
+  });
+  const size_t nl = static_cast<size_t>(84) * 1000 * 1000 / 16;  // one decode layer's state
+  int layer = 0;
+  hbm("in-place 84 MB, 4 rotating buffers", 2.0 * nl * 16, [&] {
+    float4* base = a + static_cast<size_t>(layer++ % 4) * nl * 2;
+    hipLaunchKernelGGL(k_inplace, dim3((nl + 255) / 256), dim3(256), 0, 0, base, nl);
+  });
+  CK(hipDeviceSynchronize());
+  std::printf("done\n");
+  return 0;
+}

@@ -48,6 +48,9 @@ SSM_FWD_INSTANCES(SSM_EXTERN_FWD)
 // Carry pass: one lane per (sequence, state n, channel d), channels fastest.
 // h runs through the chunk summaries in order, h <- e^(A[d,n] S_c) h + H_c,
 // and each slot of ws_H is overwritten with the state entering chunk c+1.
+// Summaries are read kCarryBatch chunks at a time, ahead of the stores that
+// overwrite them, so the loads of a batch are in flight together.
+constexpr int kCarryBatch = 32;
 __global__ void __launch_bounds__(256) fwd_carry_kernel(const float* __restrict__ A,
                                                         const float* __restrict__ h0,
                                                         const float* __restrict__ ws_S,
@@ -61,13 +64,26 @@ __global__ void __launch_bounds__(256) fwd_carry_kernel(const float* __restrict_
   const float an = A[static_cast<size_t>(d) * N + n];
   float h = h0 ? h0[(b * dim + d) * N + n] : 0.0f;
   const size_t slot0 = static_cast<size_t>(b) * (K - 1);
-  for (int c = 0; c < K - 1; ++c) {
-    const size_t slot = slot0 + c;
-    const float S = ws_S[slot * dim + d];
-    float* hp = ws_H + (slot * N + n) * dim + d;
-    float unused;
-    h = __builtin_fmaf(exp_acc(an * S, unused), h, *hp);
-    *hp = h;
+  const size_t sstride = static_cast<size_t>(dim), hstride = static_cast<size_t>(N) * dim;
+  const float* sp = ws_S + slot0 * sstride + d;
+  float* hp = ws_H + (slot0 * N + n) * dim + d;
+  for (int c0 = 0; c0 < K - 1; c0 += kCarryBatch) {
+    const int m = (K - 1 - c0 < kCarryBatch) ? K - 1 - c0 : kCarryBatch;
+    float Sv[kCarryBatch], Hv[kCarryBatch];
+#pragma unroll
+    for (int j = 0; j < kCarryBatch; ++j) {
+      const int jj = j < m ? j : m - 1;
+      Sv[j] = sp[(c0 + jj) * sstride];
+      Hv[j] = hp[(c0 + jj) * hstride];
+    }
+#pragma unroll
+    for (int j = 0; j < kCarryBatch; ++j) {
+      if (j < m) {
+        float unused;
+        h = __builtin_fmaf(exp_acc(an * Sv[j], unused), h, Hv[j]);
+        hp[(c0 + j) * hstride] = h;
+      }
+    }
   }
 }
 
@@ -142,6 +158,113 @@ __global__ void __launch_bounds__(256) decode_vec_kernel(DecArgs<TA> a) {
   }
 }
 
+// NT values of a B or C row as 16-byte vector loads (row start 16-byte aligned).
+template <int NT>
+__device__ __forceinline__ void load_row16(const float* p, float (&v)[NT]) {
+  const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+  for (int i = 0; i < NT / 4; ++i) {
+    const float4 w = q[i];
+    v[4 * i] = w.x; v[4 * i + 1] = w.y; v[4 * i + 2] = w.z; v[4 * i + 3] = w.w;
+  }
+}
+template <int NT>
+__device__ __forceinline__ void load_row16(const bf16_t* p, float (&v)[NT]) {
+  static_assert(NT % 4 == 0, "");
+  const uint2* q = reinterpret_cast<const uint2*>(p);  // 4 bf16 per 8 bytes
+#pragma unroll
+  for (int i = 0; i < NT / 4; ++i) {
+    const uint2 w = q[i];
+    v[4 * i] = __uint_as_float(w.x << 16);
+    v[4 * i + 1] = __uint_as_float(w.x & 0xffff0000u);
+    v[4 * i + 2] = __uint_as_float(w.y << 16);
+    v[4 * i + 3] = __uint_as_float(w.y & 0xffff0000u);
+  }
+}
+
+// dstate in {4, 8, 16}: one lane per (sequence, channel).  A block's state
+// tile (256 channels x N floats, contiguous in memory) moves between HBM and
+// LDS with fully coalesced 16-byte accesses; each lane then works on its own
+// channel's row from LDS, so softplus, the gate and the exponentials are
+// computed once per channel.  When the channel's A has the S4D-real shape
+// A[n] = (n+1) A[0], the decays are powers of r = e^(Delta A[0]) taken
+// against r's two-float value (one accurate exponential per channel).
+constexpr int kDecBlock = 256;
+template <typename TA, int NT>
+__global__ void __launch_bounds__(kDecBlock) decode_chan_kernel(DecArgs<TA> a) {
+  static_assert(NT % 4 == 0 && NT <= 16, "whole float4 rows");
+  constexpr int Q = NT / 4;            // float4 per row
+  constexpr int ROW = NT + 4;          // LDS row stride in floats (padding spreads banks)
+  __shared__ float4 tile[kDecBlock * ROW / 4];
+  const int64_t nch = a.batch * a.dim;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kDecBlock;
+  const int t = threadIdx.x;
+  const int nrows = static_cast<int>((nch - c0) < kDecBlock ? (nch - c0) : kDecBlock);
+  const float4* gst = reinterpret_cast<const float4*>(a.state + c0 * NT);
+  // coalesced load of the tile: float4 f = row f/Q, quad f%Q
+#pragma unroll
+  for (int k = 0; k < Q; ++k) {
+    const int f = t + k * kDecBlock;
+    if (f < nrows * Q) tile[(f / Q) * (ROW / 4) + (f % Q)] = gst[f];
+  }
+  __syncthreads();
+  const bool valid = t < nrows;
+  const int64_t c = c0 + (valid ? t : 0);
+  const int64_t b = c / a.dim;
+  const int d = static_cast<int>(c % a.dim);
+  float h[NT], Av[NT], Bv[NT], Cv[NT];
+  const float4* ap = reinterpret_cast<const float4*>(a.A + static_cast<size_t>(d) * NT);
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const float4 v = tile[t * (ROW / 4) + q];
+    const float4 w = ap[q];
+    h[4 * q] = v.x; h[4 * q + 1] = v.y; h[4 * q + 2] = v.z; h[4 * q + 3] = v.w;
+    Av[4 * q] = w.x; Av[4 * q + 1] = w.y; Av[4 * q + 2] = w.z; Av[4 * q + 3] = w.w;
+  }
+  // B and C rows of this sequence with 16-byte loads (rows are 16-byte aligned)
+  load_row16<NT>(a.B + b * NT, Bv);
+  load_row16<NT>(a.C + b * NT, Cv);
+  const float xv = to_f32(a.x[c]);
+  const float raw = to_f32(a.delta[c]) + (a.bias ? a.bias[d] : 0.0f);
+  const float dt = a.softplus ? softplus_f32(raw) : raw;
+  const float dx = dt * xv;
+  bool pow_ok = true;
+#pragma unroll
+  for (int n = 1; n < NT; ++n) pow_ok = pow_ok && (Av[n] == static_cast<float>(n + 1) * Av[0]);
+  float y = 0.0f;
+  if (__all(pow_ok)) {
+    float rl;
+    const float rh = exp_acc(dt * Av[0], rl);
+    float p = rh;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      h[n] = __builtin_fmaf(p, h[n], dx * Bv[n]);
+      y = __builtin_fmaf(Cv[n], h[n], y);
+      if (n + 1 < NT) p = __builtin_fmaf(p, rh, p * rl);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      float unused;
+      h[n] = __builtin_fmaf(exp_acc(dt * Av[n], unused), h[n], dx * Bv[n]);
+      y = __builtin_fmaf(Cv[n], h[n], y);
+    }
+  }
+  y += (a.Dsk ? a.Dsk[d] : 0.0f) * xv;
+  if (a.z) y *= silu_f32(to_f32(a.z[c]));
+  if (valid) store_act(a.out + c, y);
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+    tile[t * (ROW / 4) + q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+  __syncthreads();
+  float4* gso = reinterpret_cast<float4*>(a.state + c0 * NT);
+#pragma unroll
+  for (int k = 0; k < Q; ++k) {
+    const int f = t + k * kDecBlock;
+    if (f < nrows * Q) gso[f] = tile[(f / Q) * (ROW / 4) + (f % Q)];
+  }
+}
+
 // Any dstate <= 64: one lane per channel, state row walked element by element.
 template <typename TA>
 __global__ void __launch_bounds__(256) decode_scalar_kernel(DecArgs<TA> a) {
@@ -212,7 +335,10 @@ void launch_carry(const float* A, const float* h0, const float* ws_S, float* ws_
 // Chunking plan: enough (channel tile x chunk) waves for about kWavesPerSimd
 // resident waves on every SIMD, chunks of a multiple of 2*kGroup tokens and
 // at least kMinChunk long.
-constexpr int kWavesPerSimd = 4;
+#ifndef SSM_WAVES_PER_SIMD
+#define SSM_WAVES_PER_SIMD 8
+#endif
+constexpr int kWavesPerSimd = SSM_WAVES_PER_SIMD;
 constexpr int kMinChunk = 32;
 
 struct Plan {
@@ -281,10 +407,15 @@ int dispatch_decode(const DecArgs<TA>& a, hipStream_t s) {
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, a);
     return launch_status("ssm_state_update");
   };
+  auto chan = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((nch + kDecBlock - 1) / kDecBlock)),
+                       dim3(kDecBlock), 0, s, a);
+    return launch_status("ssm_state_update");
+  };
   switch (a.N) {
-    case 4: return vec(decode_vec_kernel<TA, 1>, 1);
-    case 8: return vec(decode_vec_kernel<TA, 2>, 2);
-    case 16: return vec(decode_vec_kernel<TA, 4>, 4);
+    case 4: return chan(decode_chan_kernel<TA, 4>);
+    case 8: return chan(decode_chan_kernel<TA, 8>);
+    case 16: return chan(decode_chan_kernel<TA, 16>);
     case 32: return vec(decode_vec_kernel<TA, 8>, 8);
     case 64: return vec(decode_vec_kernel<TA, 16>, 16);
     default: {
@@ -423,8 +554,10 @@ int ssm_state_update(float* state, const void* x, const void* delta, const float
   for (const auto& e : al)
     if (e.p && !aligned(e.p, e.k))
       return fail(SSM_ERR_ALIGN, "ssm_state_update: %s is not %zu-byte aligned", e.n, e.k);
-  if (dstate % 4 == 0 && !aligned(A, 16))
-    return fail(SSM_ERR_ALIGN, "ssm_state_update: A must be 16-byte aligned when dstate %% 4 == 0");
+  if (dstate % 4 == 0 && (!aligned(A, 16) || !aligned(B, 4 * es) || !aligned(C, 4 * es)))
+    return fail(SSM_ERR_ALIGN,
+                "ssm_state_update: with dstate %% 4 == 0, A must be 16-byte aligned and B, C aligned "
+                "to 4 elements");
   const size_t tok = static_cast<size_t>(batch) * dim * es;
   const size_t bc = static_cast<size_t>(batch) * dstate * es;
   const size_t st = static_cast<size_t>(batch) * dim * dstate * 4;
