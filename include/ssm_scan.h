@@ -38,8 +38,9 @@
  *     synchronisation, as for any HIP kernel.
  *   - Alignment: act tensors must be aligned to their element size; A, D_skip,
  *     delta_bias to 4 bytes; B and C to 4 bytes; state tensors to 16 bytes.
- *   - Outputs may not overlap inputs, except that last_state may be the same
- *     buffer as initial_state (resume in place).
+ *   - Outputs may not overlap inputs (nor the workspace), except that in
+ *     ssm_scan_fwd last_state may be the same buffer as initial_state
+ *     (resume in place).
  *   - Not thread-hostile: concurrent calls on different streams are fine.
  */
 #ifndef SSM_SCAN_H
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 1
+#define SSM_SCAN_ABI_VERSION 2
 
 typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
 
@@ -99,6 +100,50 @@ int ssm_scan_fwd(const void* x, const void* delta, const float* delta_bias, int 
  * (0 when none is needed).  Never fails; returns 0 for invalid sizes. */
 size_t ssm_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                                     int dtype);
+
+/*
+ * Forward selective scan over packed variable-length sequences.
+ * Padding a batch of unequal sequences on the right feeds the padding tokens
+ * through the recurrence and changes the state they leave behind; the
+ * remedy that "Linear Attention vs Softmax Attention: Can RWKV or Mamba
+ * Replace Transformers?" (shyankdev.com) gives in "Common Mistakes" (mistake
+ * 1 and "1. Naive Sequence Padding in Batched Training") and in "Best
+ * Practices" (item 4) is to concatenate the sequences without padding and
+ * pass their offsets.  Each sequence starts from its own state, as in the
+ * same page's "State Reset and Isolation" (section "Production Deployment
+ * Considerations", item 2).
+ *   x, delta, z, out : (total_len, dim) act, the sequences one after another
+ *   B, C             : (total_len, dstate) act
+ *   cu_seqlens       : (nseq + 1) int32 DEVICE array of token offsets:
+ *                      sequence s is tokens [cu_seqlens[s], cu_seqlens[s+1]);
+ *                      must satisfy 0 = cu[0] <= cu[1] <= ... <= cu[nseq] =
+ *                      total_len (empty sequences are allowed).  The contents
+ *                      are not checked (that would need a synchronisation):
+ *                      offsets that break this rule give unspecified values
+ *                      but every memory access stays inside the buffers.
+ *   initial_state    : (nseq, dim, dstate) float32 or NULL (= zeros)
+ *   last_state       : (nseq, dim, dstate) float32 or NULL; receives each
+ *                      sequence's state after its last token (its initial
+ *                      state if it is empty).  May not overlap initial_state.
+ *   A, D_skip, delta_bias, delta_softplus, dtype : as in ssm_scan_fwd.
+ *   1 <= nseq <= 2^24; total_len >= 0.
+ *   workspace        : at least ssm_scan_fwd_varlen_workspace_bytes(...)
+ *                      bytes, 256-byte aligned, as in ssm_scan_fwd.
+ * Each sequence's out and last_state equal those of ssm_scan_fwd run on that
+ * sequence alone (batch = 1) with its initial state, up to float32 rounding
+ * order.
+ */
+int ssm_scan_fwd_varlen(const void* x, const void* delta, const float* delta_bias,
+                        int delta_softplus, const float* A, const void* B, const void* C,
+                        const float* D_skip, const void* z, void* out, float* last_state,
+                        const float* initial_state, const int32_t* cu_seqlens, int64_t nseq,
+                        int64_t total_len, int64_t dim, int64_t dstate, int dtype,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace size ssm_scan_fwd_varlen needs (0 when none is needed, or for
+ * invalid sizes). */
+size_t ssm_scan_fwd_varlen_workspace_bytes(int64_t nseq, int64_t total_len, int64_t dim,
+                                           int64_t dstate, int dtype);
 
 /*
  * One decoding step for `batch` sequences: the recurrence above with one token.

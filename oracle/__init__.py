@@ -3,4 +3,4 @@
 Only tests, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline``
 leg may import this package.  The product path never does.
 """
-from .oracle import build, scan, state_update, oracle_lib_path  # noqa: F401
+from .oracle import build, scan, scan_varlen, state_update, oracle_lib_path  # noqa: F401

@@ -128,3 +128,37 @@ def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, delt
                      z=r(z, (batch, 1, dim)), delta_bias=delta_bias,
                      delta_softplus=delta_softplus, h0=state, nthreads=nthreads)
     return out[:, 0, :], last
+
+
+def scan_varlen(x, delta, A, B, C, cu_seqlens, D=None, z=None, delta_bias=None,
+                delta_softplus=True, h0=None, want_last_state=True, nthreads=None):
+    """Packed variable-length sequences: the sequences are independent, each
+    runs the scan above from its own initial state.
+
+    x, delta, z: (total, dim); B, C: (total, N); cu_seqlens: nseq + 1 token
+    offsets (sequence s is rows [cu[s], cu[s+1])); h0: (nseq, dim, N).
+    Returns (out (total, dim), last_state (nseq, dim, N)) in float64.
+    Follows "Linear Attention vs Softmax Attention: Can RWKV or Mamba Replace
+    Transformers?", "Common Mistakes" and "Best Practices" item 4 (sequences
+    concatenated without padding, with offsets) and "State Reset and
+    Isolation" (each sequence starts from its own state).
+    """
+    cu = [int(v) for v in np.asarray(cu_seqlens).reshape(-1)]
+    nseq = len(cu) - 1
+    x = np.asarray(x, dtype=np.float32)
+    total, dim = x.shape
+    N = np.asarray(A).shape[1]
+    if nseq < 1 or cu[0] != 0 or cu[-1] != total or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must rise from 0 to total")
+    tok = lambda a, s: None if a is None else np.asarray(a, dtype=np.float32)[cu[s]:cu[s + 1]][None]
+    out = np.empty((total, dim), dtype=np.float64)
+    last = np.empty((nseq, dim, N), dtype=np.float64) if want_last_state else None
+    for s in range(nseq):
+        o, l = scan(tok(x, s), tok(delta, s), A, tok(B, s), tok(C, s), D=D, z=tok(z, s),
+                    delta_bias=delta_bias, delta_softplus=delta_softplus,
+                    h0=None if h0 is None else np.asarray(h0, dtype=np.float32)[s:s + 1],
+                    want_last_state=True, nthreads=nthreads)
+        out[cu[s]:cu[s + 1]] = o[0]
+        if last is not None:
+            last[s] = l[0]
+    return out, last

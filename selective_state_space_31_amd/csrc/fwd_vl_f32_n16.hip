@@ -1,0 +1,7 @@
+// fwd_vl_f32_n16.hip -- instantiates the forward launchers (packed variable-length sequences) for: float N=16
+#include "kernels.hpp"
+
+namespace ssm {
+template int launch_fwd_flags<float, 16, true, true>(const FwdArgs<float>&, int64_t, bool,
+                                                  bool, hipStream_t);
+}  // namespace ssm

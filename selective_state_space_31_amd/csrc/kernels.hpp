@@ -179,6 +179,13 @@ __device__ __forceinline__ void fma_inplace(float& h, float a, float b) {
 //   scan  : per chunk, the recurrence from its entering state, with the
 //           readout, skip, gate and store fused in.
 // With K = 1 only the scan runs.
+//
+// Packed variable-length sequences (cu != NULL) run as one long sequence of
+// L = total tokens; the offsets cu[0..nseq] cut it into sequences, and at
+// each sequence start the state is set to that sequence's initial state
+// (or zero) instead of being carried.  A chunk that holds a start then has
+// the summary "forget the incoming state, end at H", which the carry pass
+// applies through the per-chunk flag F.
 // ----------------------------------------------------------------------------
 template <typename TA>
 struct FwdArgs {
@@ -194,8 +201,12 @@ struct FwdArgs {
   float* last_state;
   const float* h0;
   float* ws_S;  // (batch, K-1, dim): sum of Delta over chunk c
-  float* ws_H;  // (batch, K-1, N, dim): chunk c's end state from zero, then (after
-                // the carry pass) the state entering chunk c+1
+  float* ws_H;  // (batch, K, N, dim): slot c+1 first holds chunk c's end state from
+                // zero (or from its last sequence start); after the carry pass slot c
+                // holds the state entering chunk c
+  int* ws_F;    // (K-1), packed sequences only: 1 if chunk c holds a sequence start
+  const int* cu;  // packed sequences: nseq+1 token offsets; NULL for (batch, L) layout
+  int nseq;
   int L;
   int Lc;
   int K;
@@ -526,38 +537,92 @@ __device__ __forceinline__ void agg_reverse(const FwdArgs<TA>& a, const Chan<NT>
   }
 }
 
-// Summary pass: block (channel tile, chunk c < K-1, sequence b).
-template <typename TA, int NT, bool EXACT, bool SP>
+// Packed sequences: the sequence that token t belongs to, the largest s in
+// [0, nseq) with cu[s] <= t (sequence s is tokens [cu[s], cu[s+1])), found by
+// a 64-way search: the wave's lanes probe 64 offsets at once, so nseq <= 64
+// takes one round of loads and each further factor of 64 one more.  Every
+// probe stays inside cu[0, nseq), so offsets that are not sorted still give
+// an index in range.  t is wave-uniform and all 64 lanes must be active.
+__device__ __forceinline__ int seq_owner(const int* cu, int nseq, int t) {
+  const int lane = static_cast<int>(threadIdx.x & 63);
+  int lo = 0, cnt = nseq;
+  for (;;) {
+    const int stride = (cnt + 63) >> 6;
+    const int i = lane * stride;
+    const bool p = i < cnt && cu[lo + i] <= t;
+    const unsigned long long m = __ballot(p);
+    const int k = m ? 63 - __builtin_clzll(m) : 0;
+    lo = __builtin_amdgcn_readfirstlane(lo + k * stride);
+    if (stride == 1) return lo;
+    cnt = (cnt - k * stride < stride) ? cnt - k * stride : stride;
+  }
+}
+
+// Lane's initial state of sequence s (zeros without one).
+template <int NT, bool EXACT>
+__device__ __forceinline__ void load_h0(const float* h0, int s, int dim, int dl, int N,
+                                        float (&h)[NT]) {
+  const float* hp = h0 ? h0 + (static_cast<size_t>(s) * dim + dl) * N : nullptr;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) h[n] = (hp && (EXACT || n < N)) ? hp[n] : 0.0f;
+}
+
+// Summary pass: block (channel tile, chunk c < K-1, sequence b).  With
+// packed sequences, a chunk in which a sequence starts is summarised from
+// its last start: the state there is that sequence's initial state, and
+// the chunk's end state no longer depends on the state entering it.
+template <typename TA, int NT, bool EXACT, bool SP, bool VL>
 __global__ void __launch_bounds__(64) fwd_agg_kernel(FwdArgs<TA> a) {
   const int d0 = blockIdx.x * 64;
   const int c = blockIdx.y;
   const int b = blockIdx.z;
   const Chan<NT> ch = load_chan<TA, NT, EXACT>(a, d0);
+  const int dl = ch.valid ? d0 + static_cast<int>(threadIdx.x) : a.dim - 1;
   float h[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) h[n] = 0.0f;
   float S = 0.0f;
   const int t_begin = c * a.Lc;  // chunks before the last are full (Lc is a multiple of 2*kGroup)
-  constexpr bool REV = EXACT && NT <= 16 && sizeof(TA) == 2 && (sizeof(TA) * NT) % 4 == 0;
-  if (ch.pow) {
-    if constexpr (REV)
-      agg_reverse<TA, NT, SP>(a, ch, b, t_begin, a.Lc, h, S);
-    else
-      run_tokens<TA, NT, EXACT, SP, false, true, true>(a, ch, b, t_begin, a.Lc, h, S);
-  } else
-    run_tokens<TA, NT, EXACT, SP, false, false, true>(a, ch, b, t_begin, a.Lc, h, S);
+  bool reset = false;
+  if constexpr (VL) {
+    const int t_end = t_begin + a.Lc;
+    const int s = seq_owner(a.cu, a.nseq, t_end - 1);
+    const int st = a.cu[s];
+    if (st >= t_begin && st < t_end) {
+      reset = true;
+      load_h0<NT, EXACT>(a.h0, s, a.dim, dl, a.N, h);
+      if (ch.pow)
+        run_tokens<TA, NT, EXACT, SP, false, true, true>(a, ch, b, st, t_end - st, h, S);
+      else
+        run_tokens<TA, NT, EXACT, SP, false, false, true>(a, ch, b, st, t_end - st, h, S);
+    }
+  }
+  if (!reset) {
+    constexpr bool REV = EXACT && NT <= 16 && sizeof(TA) == 2 && (sizeof(TA) * NT) % 4 == 0;
+    if (ch.pow) {
+      if constexpr (REV)
+        agg_reverse<TA, NT, SP>(a, ch, b, t_begin, a.Lc, h, S);
+      else
+        run_tokens<TA, NT, EXACT, SP, false, true, true>(a, ch, b, t_begin, a.Lc, h, S);
+    } else
+      run_tokens<TA, NT, EXACT, SP, false, false, true>(a, ch, b, t_begin, a.Lc, h, S);
+  }
   if (ch.valid) {
     const int d = d0 + threadIdx.x;
-    const size_t slot = static_cast<size_t>(b) * (a.K - 1) + c;
-    a.ws_S[slot * a.dim + d] = S;
+    a.ws_S[(static_cast<size_t>(b) * (a.K - 1) + c) * a.dim + d] = S;
+    const size_t slot = static_cast<size_t>(b) * a.K + c + 1;
 #pragma unroll
     for (int n = 0; n < NT; ++n)
       if (EXACT || n < a.N) a.ws_H[(slot * a.N + n) * a.dim + d] = h[n];
   }
+  if (VL && blockIdx.x == 0 && threadIdx.x == 0) a.ws_F[c] = reset ? 1 : 0;
 }
 
-// Output pass: block (channel tile, chunk c, sequence b).
-template <typename TA, int NT, bool EXACT, bool SP, bool GATE>
+// Output pass: block (channel tile, chunk c, sequence b).  With packed
+// sequences the chunk is walked segment by segment (the parts of it that
+// belong to one sequence): the state is reset at each sequence start and
+// stored to last_state at each sequence end.
+template <typename TA, int NT, bool EXACT, bool SP, bool GATE, bool VL>
 __global__ void __launch_bounds__(64) fwd_scan_kernel(FwdArgs<TA> a) {
   const int d0 = blockIdx.x * 64;
   const int c = blockIdx.y;
@@ -567,35 +632,53 @@ __global__ void __launch_bounds__(64) fwd_scan_kernel(FwdArgs<TA> a) {
   const int d = d0 + threadIdx.x;
   const int dl = ch.valid ? d : a.dim - 1;
   float h[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) h[n] = 0.0f;
-  if (c == 0) {
-    if (a.h0) {
-      const float* hp = a.h0 + (static_cast<size_t>(b) * a.dim + dl) * N;
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-        if (EXACT || n < N) h[n] = hp[n];
-    }
-  } else {
-    const size_t slot = static_cast<size_t>(b) * (a.K - 1) + (c - 1);
+  if (a.K > 1) {
+    // state entering the chunk, left by the carry pass (also for c = 0, so
+    // that this pass never reads initial_state, which may be last_state)
+    const size_t slot = static_cast<size_t>(b) * a.K + c;
 #pragma unroll
     for (int n = 0; n < NT; ++n)
-      if (EXACT || n < N) h[n] = a.ws_H[(slot * N + n) * a.dim + dl];
+      h[n] = (EXACT || n < N) ? a.ws_H[(slot * N + n) * a.dim + dl] : 0.0f;
+  } else {
+    load_h0<NT, EXACT>(VL ? nullptr : a.h0, b, a.dim, dl, N, h);
   }
   const int t_begin = c * a.Lc;
   const int len = (a.L - t_begin < a.Lc) ? a.L - t_begin : a.Lc;
   float S = 0.0f;
-  if (len > 0) {  // an empty sequence only carries the initial state through
-    if (ch.pow)
-      run_tokens<TA, NT, EXACT, SP, GATE, true, false>(a, ch, b, t_begin, len, h, S);
-    else
-      run_tokens<TA, NT, EXACT, SP, GATE, false, false>(a, ch, b, t_begin, len, h, S);
-  }
-  if (a.last_state && ch.valid && c == a.K - 1) {
-    float* lp = a.last_state + (static_cast<size_t>(b) * a.dim + d) * N;
+  if constexpr (!VL) {
+    if (len > 0) {  // an empty sequence only carries the initial state through
+      if (ch.pow)
+        run_tokens<TA, NT, EXACT, SP, GATE, true, false>(a, ch, b, t_begin, len, h, S);
+      else
+        run_tokens<TA, NT, EXACT, SP, GATE, false, false>(a, ch, b, t_begin, len, h, S);
+    }
+    if (a.last_state && ch.valid && c == a.K - 1) {
+      float* lp = a.last_state + (static_cast<size_t>(b) * a.dim + d) * N;
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      if (EXACT || n < N) lp[n] = h[n];
+      for (int n = 0; n < NT; ++n)
+        if (EXACT || n < N) lp[n] = h[n];
+    }
+  } else {
+    const int t_end = t_begin + (len > 0 ? len : 0);
+    int t = t_begin;
+    while (t < t_end) {
+      const int s = seq_owner(a.cu, a.nseq, t);
+      const int st = a.cu[s], en = a.cu[s + 1];
+      int e = en < t_end ? en : t_end;
+      if (e <= t) e = t + 1;  // (offsets not sorted: still move on)
+      if (st == t) load_h0<NT, EXACT>(a.h0, s, a.dim, dl, N, h);
+      if (ch.pow)
+        run_tokens<TA, NT, EXACT, SP, GATE, true, false>(a, ch, 0, t, e - t, h, S);
+      else
+        run_tokens<TA, NT, EXACT, SP, GATE, false, false>(a, ch, 0, t, e - t, h, S);
+      if (a.last_state && ch.valid && e == en) {
+        float* lp = a.last_state + (static_cast<size_t>(s) * a.dim + d) * N;
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          if (EXACT || n < N) lp[n] = h[n];
+      }
+      t = e;
+    }
   }
 }
 
@@ -603,32 +686,37 @@ __global__ void __launch_bounds__(64) fwd_scan_kernel(FwdArgs<TA> a) {
 // launchers (host side of the templates above)
 // ----------------------------------------------------------------------------
 int launch_status(const char* what);
-void launch_carry(const float* A, const float* h0, const float* ws_S, float* ws_H, int64_t batch,
-                  int dim, int N, int K, hipStream_t s);
+void launch_carry(const float* A, const float* h0, const float* ws_S, float* ws_H,
+                  const int* ws_F, int64_t batch, int dim, int N, int K, hipStream_t s);
+void launch_varlen_empty(const int* cu, int nseq, const float* h0, float* last_state, int dim,
+                         int N, hipStream_t s);
 
-template <typename TA, int NT, bool EXACT, bool SP, bool GATE>
+template <typename TA, int NT, bool EXACT, bool SP, bool GATE, bool VL>
 int launch_fwd(const FwdArgs<TA>& a, int64_t batch, hipStream_t s) {
   const unsigned tiles = static_cast<unsigned>((a.dim + 63) / 64);
   if (a.K > 1) {
-    hipLaunchKernelGGL((fwd_agg_kernel<TA, NT, EXACT, SP>),
+    hipLaunchKernelGGL((fwd_agg_kernel<TA, NT, EXACT, SP, VL>),
                        dim3(tiles, static_cast<unsigned>(a.K - 1), static_cast<unsigned>(batch)),
                        dim3(64), 0, s, a);
-    launch_carry(a.A, a.h0, a.ws_S, a.ws_H, batch, a.dim, a.N, a.K, s);
+    launch_carry(a.A, VL ? nullptr : a.h0, a.ws_S, a.ws_H, VL ? a.ws_F : nullptr, batch, a.dim,
+                 a.N, a.K, s);
   }
-  hipLaunchKernelGGL((fwd_scan_kernel<TA, NT, EXACT, SP, GATE>),
-                     dim3(tiles, static_cast<unsigned>(a.K), static_cast<unsigned>(batch)),
-                     dim3(64), 0, s, a);
-  return launch_status("ssm_scan_fwd");
+  if (!VL || a.L > 0)
+    hipLaunchKernelGGL((fwd_scan_kernel<TA, NT, EXACT, SP, GATE, VL>),
+                       dim3(tiles, static_cast<unsigned>(a.K), static_cast<unsigned>(batch)),
+                       dim3(64), 0, s, a);
+  // empty packed sequences: last_state = initial state (no token writes it)
+  if (VL && a.last_state) launch_varlen_empty(a.cu, a.nseq, a.h0, a.last_state, a.dim, a.N, s);
+  return launch_status(VL ? "ssm_scan_fwd_varlen" : "ssm_scan_fwd");
 }
 
-template <typename TA, int NT, bool EXACT>
+template <typename TA, int NT, bool EXACT, bool VL>
 int launch_fwd_flags(const FwdArgs<TA>& a, int64_t batch, bool sp, bool gate, hipStream_t s) {
   if (sp)
-    return gate ? launch_fwd<TA, NT, EXACT, true, true>(a, batch, s)
-                : launch_fwd<TA, NT, EXACT, true, false>(a, batch, s);
-  return gate ? launch_fwd<TA, NT, EXACT, false, true>(a, batch, s)
-              : launch_fwd<TA, NT, EXACT, false, false>(a, batch, s);
+    return gate ? launch_fwd<TA, NT, EXACT, true, true, VL>(a, batch, s)
+                : launch_fwd<TA, NT, EXACT, true, false, VL>(a, batch, s);
+  return gate ? launch_fwd<TA, NT, EXACT, false, true, VL>(a, batch, s)
+              : launch_fwd<TA, NT, EXACT, false, false, VL>(a, batch, s);
 }
-
 
 }  // namespace ssm

@@ -40,22 +40,27 @@ namespace ssm {
   X(float, 4, false) X(float, 16, false) X(float, 64, false)                       \
   X(bf16_t, 4, true) X(bf16_t, 8, true) X(bf16_t, 16, true) X(bf16_t, 32, true)    \
   X(bf16_t, 4, false) X(bf16_t, 16, false) X(bf16_t, 64, false)
-#define SSM_EXTERN_FWD(TA, NT, EX)                                                 \
-  extern template int launch_fwd_flags<TA, NT, EX>(const FwdArgs<TA>&, int64_t, bool, bool, \
-                                                   hipStream_t);
+#define SSM_EXTERN_FWD(TA, NT, EX)                                                     \
+  extern template int launch_fwd_flags<TA, NT, EX, false>(const FwdArgs<TA>&, int64_t, bool,  \
+                                                          bool, hipStream_t);                 \
+  extern template int launch_fwd_flags<TA, NT, EX, true>(const FwdArgs<TA>&, int64_t, bool,   \
+                                                         bool, hipStream_t);
 SSM_FWD_INSTANCES(SSM_EXTERN_FWD)
 
 // Carry pass: one lane per (sequence, state n, channel d), channels fastest.
-// h runs through the chunk summaries in order, h <- e^(A[d,n] S_c) h + H_c,
-// and each slot of ws_H is overwritten with the state entering chunk c+1.
-// Summaries are read kCarryBatch chunks at a time, ahead of the stores that
-// overwrite them, so the loads of a batch are in flight together.
+// Slot 0 of ws_H receives the initial state; then h runs through the chunk
+// summaries in order, h <- e^(A[d,n] S_c) h + H_c (or h <- H_c where the flag
+// F_c marks a chunk that holds a packed-sequence start), and slot c+1 is
+// overwritten with the state entering chunk c+1.  Summaries are read
+// kCarryBatch chunks at a time, ahead of the stores that overwrite them, so
+// the loads of a batch are in flight together.
 constexpr int kCarryBatch = 32;
 __global__ void __launch_bounds__(256) fwd_carry_kernel(const float* __restrict__ A,
                                                         const float* __restrict__ h0,
                                                         const float* __restrict__ ws_S,
-                                                        float* __restrict__ ws_H, int64_t batch,
-                                                        int dim, int N, int K) {
+                                                        float* __restrict__ ws_H,
+                                                        const int* __restrict__ ws_F,
+                                                        int64_t batch, int dim, int N, int K) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= batch * N * dim) return;
   const int d = static_cast<int>(idx % dim);
@@ -63,28 +68,47 @@ __global__ void __launch_bounds__(256) fwd_carry_kernel(const float* __restrict_
   const int64_t b = idx / (static_cast<int64_t>(dim) * N);
   const float an = A[static_cast<size_t>(d) * N + n];
   float h = h0 ? h0[(b * dim + d) * N + n] : 0.0f;
-  const size_t slot0 = static_cast<size_t>(b) * (K - 1);
   const size_t sstride = static_cast<size_t>(dim), hstride = static_cast<size_t>(N) * dim;
-  const float* sp = ws_S + slot0 * sstride + d;
-  float* hp = ws_H + (slot0 * N + n) * dim + d;
+  const float* sp = ws_S + static_cast<size_t>(b) * (K - 1) * sstride + d;
+  float* hp = ws_H + (static_cast<size_t>(b) * K * N + n) * dim + d;  // slot 0
+  hp[0] = h;
+  hp += hstride;  // slot c+1 <- chunk c
   for (int c0 = 0; c0 < K - 1; c0 += kCarryBatch) {
     const int m = (K - 1 - c0 < kCarryBatch) ? K - 1 - c0 : kCarryBatch;
     float Sv[kCarryBatch], Hv[kCarryBatch];
+    int Fv[kCarryBatch];
 #pragma unroll
     for (int j = 0; j < kCarryBatch; ++j) {
       const int jj = j < m ? j : m - 1;
       Sv[j] = sp[(c0 + jj) * sstride];
       Hv[j] = hp[(c0 + jj) * hstride];
+      Fv[j] = ws_F ? ws_F[c0 + jj] : 0;
     }
 #pragma unroll
     for (int j = 0; j < kCarryBatch; ++j) {
       if (j < m) {
         float unused;
-        h = __builtin_fmaf(exp_acc(an * Sv[j], unused), h, Hv[j]);
+        const float carried = __builtin_fmaf(exp_acc(an * Sv[j], unused), h, Hv[j]);
+        h = Fv[j] ? Hv[j] : carried;
         hp[(c0 + j) * hstride] = h;
       }
     }
   }
+}
+
+// Packed sequences with no tokens: last_state = initial state (or zeros).
+// Block (s, part): the blocks of a sequence that has tokens leave at once.
+__global__ void __launch_bounds__(256) fwd_varlen_empty_kernel(const int* __restrict__ cu,
+                                                               const float* __restrict__ h0,
+                                                               float* __restrict__ last_state,
+                                                               int dim, int N) {
+  const int s = blockIdx.x;
+  if (cu[s + 1] > cu[s]) return;
+  const size_t per = static_cast<size_t>(dim) * N;
+  const size_t base = static_cast<size_t>(s) * per;
+  for (size_t i = static_cast<size_t>(blockIdx.y) * 256 + threadIdx.x; i < per;
+       i += static_cast<size_t>(gridDim.y) * 256)
+    last_state[base + i] = h0 ? h0[base + i] : 0.0f;
 }
 
 // ----------------------------------------------------------------------------
@@ -325,11 +349,20 @@ int launch_status(const char* what) {
   return SSM_OK;
 }
 
-void launch_carry(const float* A, const float* h0, const float* ws_S, float* ws_H, int64_t batch,
-                  int dim, int N, int K, hipStream_t s) {
+void launch_carry(const float* A, const float* h0, const float* ws_S, float* ws_H,
+                  const int* ws_F, int64_t batch, int dim, int N, int K, hipStream_t s) {
   const int64_t lanes = batch * N * dim;
   hipLaunchKernelGGL(fwd_carry_kernel, dim3(static_cast<unsigned>((lanes + 255) / 256)), dim3(256),
-                     0, s, A, h0, ws_S, ws_H, batch, dim, N, K);
+                     0, s, A, h0, ws_S, ws_H, ws_F, batch, dim, N, K);
+}
+
+void launch_varlen_empty(const int* cu, int nseq, const float* h0, float* last_state, int dim,
+                         int N, hipStream_t s) {
+  const int64_t per = static_cast<int64_t>(dim) * N;
+  const int64_t parts = (per + 255) / 256;
+  hipLaunchKernelGGL(fwd_varlen_empty_kernel,
+                     dim3(static_cast<unsigned>(nseq), static_cast<unsigned>(parts < 16 ? parts : 16)),
+                     dim3(256), 0, s, cu, h0, last_state, dim, N);
 }
 
 // Chunking plan: enough (channel tile x chunk) waves for about kWavesPerSimd
@@ -374,28 +407,43 @@ Plan plan_fwd(int64_t batch, int64_t L, int64_t dim) {
   return p;
 }
 
-size_t workspace_for(int64_t batch, int64_t dim, int64_t N, const Plan& p) {
-  if (p.K <= 1) return 0;
-  const size_t slots = static_cast<size_t>(batch) * (p.K - 1);
-  const size_t sbytes = (slots * dim * 4 + 255) / 256 * 256;
-  return sbytes + slots * N * dim * 4;
+// Workspace: ws_S (batch, K-1, dim), then ws_H (batch, K, N, dim), then ws_F
+// (K-1 ints, packed sequences only), each part 256-byte aligned.
+struct WsLayout {
+  size_t s_off, h_off, f_off, total;
+};
+
+WsLayout workspace_layout(int64_t batch, int64_t dim, int64_t N, const Plan& p, bool varlen) {
+  WsLayout w{0, 0, 0, 0};
+  if (p.K <= 1) return w;
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  w.h_off = up(static_cast<size_t>(batch) * (p.K - 1) * dim * 4);
+  w.f_off = up(w.h_off + static_cast<size_t>(batch) * p.K * N * dim * 4);
+  w.total = varlen ? w.f_off + static_cast<size_t>(p.K - 1) * 4 : w.f_off;
+  return w;
 }
 
-template <typename TA>
-int dispatch_fwd(const FwdArgs<TA>& a, int64_t batch, bool sp, hipStream_t s) {
+template <typename TA, bool VL>
+int dispatch_fwd_vl(const FwdArgs<TA>& a, int64_t batch, bool sp, hipStream_t s) {
   const bool gate = a.z != nullptr;
   switch (a.N) {
-    case 16: return launch_fwd_flags<TA, 16, true>(a, batch, sp, gate, s);
-    case 8: return launch_fwd_flags<TA, 8, true>(a, batch, sp, gate, s);
-    case 4: return launch_fwd_flags<TA, 4, true>(a, batch, sp, gate, s);
-    case 32: return launch_fwd_flags<TA, 32, true>(a, batch, sp, gate, s);
+    case 16: return launch_fwd_flags<TA, 16, true, VL>(a, batch, sp, gate, s);
+    case 8: return launch_fwd_flags<TA, 8, true, VL>(a, batch, sp, gate, s);
+    case 4: return launch_fwd_flags<TA, 4, true, VL>(a, batch, sp, gate, s);
+    case 32: return launch_fwd_flags<TA, 32, true, VL>(a, batch, sp, gate, s);
     default: break;
   }
   // other state sizes (and 64, whose fully unrolled exact form compiles very
   // slowly) run padded with zero states up to the next supported width
-  if (a.N < 4) return launch_fwd_flags<TA, 4, false>(a, batch, sp, gate, s);
-  if (a.N < 16) return launch_fwd_flags<TA, 16, false>(a, batch, sp, gate, s);
-  return launch_fwd_flags<TA, 64, false>(a, batch, sp, gate, s);
+  if (a.N < 4) return launch_fwd_flags<TA, 4, false, VL>(a, batch, sp, gate, s);
+  if (a.N < 16) return launch_fwd_flags<TA, 16, false, VL>(a, batch, sp, gate, s);
+  return launch_fwd_flags<TA, 64, false, VL>(a, batch, sp, gate, s);
+}
+
+template <typename TA>
+int dispatch_fwd(const FwdArgs<TA>& a, int64_t batch, bool sp, hipStream_t s) {
+  return a.cu ? dispatch_fwd_vl<TA, true>(a, batch, sp, s)
+              : dispatch_fwd_vl<TA, false>(a, batch, sp, s);
 }
 
 template <typename TA>
@@ -428,6 +476,101 @@ int dispatch_decode(const DecArgs<TA>& a, hipStream_t s) {
 
 constexpr int64_t kMaxDim = (int64_t{1} << 24);   // rows of a token group stay < 4 GiB
 constexpr int64_t kMaxLen = (int64_t{1} << 31) - 64;
+constexpr int64_t kMaxSeqs = (int64_t{1} << 24);  // packed sequences per call
+
+// Checks and launch shared by both forward entry points.  Dense layout:
+// `batch` sequences of `seqlen` tokens, cu == NULL.  Packed layout: one row
+// of seqlen = total tokens cut by cu into nseq sequences (batch is 1).
+// States are (nstate, dim, dstate) with nstate = batch or nseq.
+int fwd_impl(const char* fn, const void* x, const void* delta, const float* delta_bias,
+             int delta_softplus, const float* A, const void* B, const void* C,
+             const float* D_skip, const void* z, void* out, float* last_state,
+             const float* initial_state, const int* cu, int64_t nseq, int64_t batch,
+             int64_t seqlen, int64_t dim, int64_t dstate, int dtype, void* workspace,
+             size_t workspace_bytes, hipStream_t stream) {
+  const bool varlen = cu != nullptr;
+  if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16)
+    return fail(SSM_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+  if (delta_softplus != 0 && delta_softplus != 1)
+    return fail(SSM_ERR_UNSUPPORTED, "%s: delta_softplus must be 0 or 1, got %d", fn,
+                delta_softplus);
+  if (batch < 1 || dim < 1 || seqlen < 0)
+    return fail(SSM_ERR_SHAPE, "%s: need batch >= 1, dim >= 1, seqlen >= 0 (got %lld, %lld, %lld)",
+                fn, (long long)batch, (long long)dim, (long long)seqlen);
+  if (varlen && (nseq < 1 || nseq > kMaxSeqs))
+    return fail(SSM_ERR_SHAPE, "%s: nseq must be in [1, %lld], got %lld", fn,
+                (long long)kMaxSeqs, (long long)nseq);
+  if (dstate < 1 || dstate > 64)
+    return fail(SSM_ERR_UNSUPPORTED, "%s: dstate must be in [1, 64], got %lld", fn,
+                (long long)dstate);
+  if (dim > kMaxDim || batch > 65535 || seqlen > kMaxLen)
+    return fail(SSM_ERR_SHAPE, "%s: dim %lld, batch %lld or seqlen %lld too large", fn,
+                (long long)dim, (long long)batch, (long long)seqlen);
+  if (seqlen > 0 && (!x || !delta || !B || !C || !out))
+    return fail(SSM_ERR_NULL, "%s: x, delta, B, C and out are required", fn);
+  if (!A) return fail(SSM_ERR_NULL, "%s: A is required", fn);
+  const size_t es = dtype == SSM_DTYPE_F32 ? 4 : 2;
+  const struct { const void* p; size_t k; const char* n; } al[] = {
+      {x, es, "x"}, {delta, es, "delta"}, {z, es, "z"}, {out, es, "out"}, {B, 4, "B"}, {C, 4, "C"},
+      {A, 4, "A"}, {D_skip, 4, "D_skip"}, {delta_bias, 4, "delta_bias"},
+      {last_state, 16, "last_state"}, {initial_state, 16, "initial_state"}, {cu, 4, "cu_seqlens"}};
+  for (const auto& e : al)
+    if (e.p && !aligned(e.p, e.k))
+      return fail(SSM_ERR_ALIGN, "%s: %s is not %zu-byte aligned", fn, e.n, e.k);
+  const int64_t nstate = varlen ? nseq : batch;
+  const size_t tok = static_cast<size_t>(batch) * seqlen * dim * es;
+  const size_t bc = static_cast<size_t>(batch) * seqlen * dstate * es;
+  const size_t st = static_cast<size_t>(nstate) * dim * dstate * 4;
+  const Span ins[] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, z ? tok : 0, "z"}, {B, bc, "B"},
+                      {C, bc, "C"}, {A, static_cast<size_t>(dim) * dstate * 4, "A"},
+                      {D_skip, D_skip ? static_cast<size_t>(dim) * 4 : 0, "D_skip"},
+                      {delta_bias, delta_bias ? static_cast<size_t>(dim) * 4 : 0, "delta_bias"},
+                      {initial_state, initial_state ? st : 0, "initial_state"},
+                      {cu, varlen ? static_cast<size_t>(nseq + 1) * 4 : 0, "cu_seqlens"}};
+  const Span outs[] = {{out, tok, "out"}, {last_state, last_state ? st : 0, "last_state"}};
+  for (const auto& o : outs)
+    for (const auto& i : ins) {
+      // dense layout: resume in place (last_state == initial_state) is allowed
+      if (!varlen && o.p == last_state && i.p == initial_state && o.p == i.p) continue;
+      if (overlap(o, i))
+        return fail(SSM_ERR_ALIAS, "%s: output %s overlaps input %s", fn, o.name, i.name);
+    }
+  if (overlap(outs[0], outs[1])) return fail(SSM_ERR_ALIAS, "%s: out overlaps last_state", fn);
+  const Plan plan = plan_fwd(batch, seqlen, dim);
+  const WsLayout wl = workspace_layout(batch, dim, dstate, plan, varlen);
+  if (workspace_bytes < wl.total || (wl.total > 0 && !workspace))
+    return fail(SSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, wl.total,
+                workspace_bytes);
+  if (wl.total > 0 && !aligned(workspace, 256))
+    return fail(SSM_ERR_ALIGN, "%s: workspace is not 256-byte aligned", fn);
+  if (overlap(Span{workspace, wl.total, "workspace"}, outs[0]) ||
+      overlap(Span{workspace, wl.total, "workspace"}, outs[1]))
+    return fail(SSM_ERR_ALIAS, "%s: workspace overlaps an output", fn);
+  for (const auto& i : ins)
+    if (overlap(Span{workspace, wl.total, "workspace"}, i))
+      return fail(SSM_ERR_ALIAS, "%s: workspace overlaps input %s", fn, i.name);
+  if (seqlen == 0 && !last_state) return SSM_OK;
+  char* wsb = static_cast<char*>(workspace);
+  float* ws_S = wl.total ? reinterpret_cast<float*>(wsb + wl.s_off) : nullptr;
+  float* ws_H = wl.total ? reinterpret_cast<float*>(wsb + wl.h_off) : nullptr;
+  int* ws_F = (wl.total && varlen) ? reinterpret_cast<int*>(wsb + wl.f_off) : nullptr;
+  const int nq = static_cast<int>(varlen ? nseq : 0);
+
+  if (dtype == SSM_DTYPE_F32) {
+    FwdArgs<float> a{static_cast<const float*>(x), static_cast<const float*>(delta), delta_bias, A,
+                     static_cast<const float*>(B), static_cast<const float*>(C), D_skip,
+                     static_cast<const float*>(z), static_cast<float*>(out), last_state,
+                     initial_state, ws_S, ws_H, ws_F, cu, nq, static_cast<int>(seqlen), plan.Lc,
+                     plan.K, static_cast<int>(dim), static_cast<int>(dstate)};
+    return dispatch_fwd(a, batch, delta_softplus != 0, stream);
+  }
+  FwdArgs<bf16_t> a{static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(delta), delta_bias, A,
+                    static_cast<const bf16_t*>(B), static_cast<const bf16_t*>(C), D_skip,
+                    static_cast<const bf16_t*>(z), static_cast<bf16_t*>(out), last_state,
+                    initial_state, ws_S, ws_H, ws_F, cu, nq, static_cast<int>(seqlen), plan.Lc,
+                    plan.K, static_cast<int>(dim), static_cast<int>(dstate)};
+  return dispatch_fwd(a, batch, delta_softplus != 0, stream);
+}
 
 }  // namespace ssm
 
@@ -445,7 +588,16 @@ size_t ssm_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
   if (batch < 1 || dim < 1 || seqlen < 0 || dstate < 1 || dstate > 64 || dim > kMaxDim ||
       batch > 65535 || seqlen > kMaxLen)
     return 0;
-  return workspace_for(batch, dim, dstate, plan_fwd(batch, seqlen, dim));
+  return workspace_layout(batch, dim, dstate, plan_fwd(batch, seqlen, dim), false).total;
+}
+
+size_t ssm_scan_fwd_varlen_workspace_bytes(int64_t nseq, int64_t total_len, int64_t dim,
+                                           int64_t dstate, int dtype) {
+  (void)dtype;
+  if (nseq < 1 || nseq > kMaxSeqs || dim < 1 || total_len < 0 || dstate < 1 || dstate > 64 ||
+      dim > kMaxDim || total_len > kMaxLen)
+    return 0;
+  return workspace_layout(1, dim, dstate, plan_fwd(1, total_len, dim), true).total;
 }
 
 int ssm_scan_fwd(const void* x, const void* delta, const float* delta_bias, int delta_softplus,
@@ -454,76 +606,22 @@ int ssm_scan_fwd(const void* x, const void* delta, const float* delta_bias, int 
                  int64_t seqlen, int64_t dim, int64_t dstate, int dtype, void* workspace,
                  size_t workspace_bytes, hipStream_t stream) {
   g_err[0] = '\0';
-  if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16)
-    return fail(SSM_ERR_UNSUPPORTED, "ssm_scan_fwd: unknown dtype %d", dtype);
-  if (delta_softplus != 0 && delta_softplus != 1)
-    return fail(SSM_ERR_UNSUPPORTED, "ssm_scan_fwd: delta_softplus must be 0 or 1, got %d",
-                delta_softplus);
-  if (batch < 1 || dim < 1 || seqlen < 0)
-    return fail(SSM_ERR_SHAPE, "ssm_scan_fwd: need batch >= 1, dim >= 1, seqlen >= 0 (got %lld, %lld, %lld)",
-                (long long)batch, (long long)dim, (long long)seqlen);
-  if (dstate < 1 || dstate > 64)
-    return fail(SSM_ERR_UNSUPPORTED, "ssm_scan_fwd: dstate must be in [1, 64], got %lld",
-                (long long)dstate);
-  if (dim > kMaxDim || batch > 65535 || seqlen > kMaxLen)
-    return fail(SSM_ERR_SHAPE, "ssm_scan_fwd: dim %lld, batch %lld or seqlen %lld too large",
-                (long long)dim, (long long)batch, (long long)seqlen);
-  if (seqlen > 0 && (!x || !delta || !B || !C || !out))
-    return fail(SSM_ERR_NULL, "ssm_scan_fwd: x, delta, B, C and out are required");
-  if (!A) return fail(SSM_ERR_NULL, "ssm_scan_fwd: A is required");
-  const size_t es = dtype == SSM_DTYPE_F32 ? 4 : 2;
-  const struct { const void* p; size_t k; const char* n; } al[] = {
-      {x, es, "x"}, {delta, es, "delta"}, {z, es, "z"}, {out, es, "out"}, {B, 4, "B"}, {C, 4, "C"},
-      {A, 4, "A"}, {D_skip, 4, "D_skip"}, {delta_bias, 4, "delta_bias"},
-      {last_state, 16, "last_state"}, {initial_state, 16, "initial_state"}};
-  for (const auto& e : al)
-    if (e.p && !aligned(e.p, e.k))
-      return fail(SSM_ERR_ALIGN, "ssm_scan_fwd: %s is not %zu-byte aligned", e.n, e.k);
-  const size_t tok = static_cast<size_t>(batch) * seqlen * dim * es;
-  const size_t bc = static_cast<size_t>(batch) * seqlen * dstate * es;
-  const size_t st = static_cast<size_t>(batch) * dim * dstate * 4;
-  const Span ins[] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, z ? tok : 0, "z"}, {B, bc, "B"},
-                      {C, bc, "C"}, {A, static_cast<size_t>(dim) * dstate * 4, "A"},
-                      {D_skip, D_skip ? static_cast<size_t>(dim) * 4 : 0, "D_skip"},
-                      {delta_bias, delta_bias ? static_cast<size_t>(dim) * 4 : 0, "delta_bias"},
-                      {initial_state, initial_state ? st : 0, "initial_state"}};
-  const Span outs[] = {{out, tok, "out"}, {last_state, last_state ? st : 0, "last_state"}};
-  for (const auto& o : outs)
-    for (const auto& i : ins) {
-      if (o.p == last_state && i.p == initial_state && o.p == i.p) continue;  // resume in place
-      if (overlap(o, i))
-        return fail(SSM_ERR_ALIAS, "ssm_scan_fwd: output %s overlaps input %s", o.name, i.name);
-    }
-  if (overlap(outs[0], outs[1]))
-    return fail(SSM_ERR_ALIAS, "ssm_scan_fwd: out overlaps last_state");
-  const Plan plan = plan_fwd(batch, seqlen, dim);
-  const size_t need = workspace_for(batch, dim, dstate, plan);
-  if (workspace_bytes < need || (need > 0 && !workspace))
-    return fail(SSM_ERR_WORKSPACE, "ssm_scan_fwd: workspace of %zu bytes needed, %zu given", need,
-                workspace_bytes);
-  if (need > 0 && !aligned(workspace, 256))
-    return fail(SSM_ERR_ALIGN, "ssm_scan_fwd: workspace is not 256-byte aligned");
-  float* ws_S = static_cast<float*>(workspace);
-  float* ws_H = need > 0 ? reinterpret_cast<float*>(
-                               static_cast<char*>(workspace) +
-                               (static_cast<size_t>(batch) * (plan.K - 1) * dim * 4 + 255) / 256 * 256)
-                         : nullptr;
-  if (seqlen == 0 && !last_state) return SSM_OK;
+  return fwd_impl("ssm_scan_fwd", x, delta, delta_bias, delta_softplus, A, B, C, D_skip, z, out,
+                  last_state, initial_state, nullptr, 0, batch, seqlen, dim, dstate, dtype,
+                  workspace, workspace_bytes, stream);
+}
 
-  if (dtype == SSM_DTYPE_F32) {
-    FwdArgs<float> a{static_cast<const float*>(x), static_cast<const float*>(delta), delta_bias, A,
-                     static_cast<const float*>(B), static_cast<const float*>(C), D_skip,
-                     static_cast<const float*>(z), static_cast<float*>(out), last_state,
-                     initial_state, ws_S, ws_H, static_cast<int>(seqlen), plan.Lc, plan.K,
-                     static_cast<int>(dim), static_cast<int>(dstate)};
-    return dispatch_fwd(a, batch, delta_softplus != 0, stream);
-  }
-  FwdArgs<bf16_t> a{static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(delta), delta_bias, A,
-                    static_cast<const bf16_t*>(B), static_cast<const bf16_t*>(C), D_skip,
-                    static_cast<const bf16_t*>(z), static_cast<bf16_t*>(out), last_state,
-                    initial_state, ws_S, ws_H, static_cast<int>(seqlen), plan.Lc, plan.K,
-                    static_cast<int>(dim), static_cast<int>(dstate)};
-  return dispatch_fwd(a, batch, delta_softplus != 0, stream);
+int ssm_scan_fwd_varlen(const void* x, const void* delta, const float* delta_bias,
+                        int delta_softplus, const float* A, const void* B, const void* C,
+                        const float* D_skip, const void* z, void* out, float* last_state,
+                        const float* initial_state, const int32_t* cu_seqlens, int64_t nseq,
+                        int64_t total_len, int64_t dim, int64_t dstate, int dtype,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (!cu_seqlens) return fail(SSM_ERR_NULL, "ssm_scan_fwd_varlen: cu_seqlens is required");
+  return fwd_impl("ssm_scan_fwd_varlen", x, delta, delta_bias, delta_softplus, A, B, C, D_skip, z,
+                  out, last_state, initial_state, cu_seqlens, nseq, 1, total_len, dim, dstate,
+                  dtype, workspace, workspace_bytes, stream);
 }
 
 int ssm_state_update(float* state, const void* x, const void* delta, const float* delta_bias,

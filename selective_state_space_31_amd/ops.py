@@ -20,7 +20,8 @@ _DTYPES = {torch.float32: SSM_DTYPE_F32, torch.bfloat16: SSM_DTYPE_BF16}
 STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL", -2: "SSM_ERR_SHAPE", -3: "SSM_ERR_UNSUPPORTED",
           -4: "SSM_ERR_ALIGN", -5: "SSM_ERR_ALIAS", -6: "SSM_ERR_WORKSPACE", -7: "SSM_ERR_HIP"}
 
-EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_state_update", "ssm_last_error",
+EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd_varlen",
+           "ssm_scan_fwd_varlen_workspace_bytes", "ssm_state_update", "ssm_last_error",
            "ssm_abi_version")
 
 
@@ -47,6 +48,11 @@ def load_library(path=LIB_PATH):
     lib.ssm_scan_fwd.restype = I
     lib.ssm_scan_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.ssm_scan_fwd_workspace_bytes.restype = SZ
+    lib.ssm_scan_fwd_varlen.argtypes = [P, P, P, I, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64,
+                                        I, P, SZ, P]
+    lib.ssm_scan_fwd_varlen.restype = I
+    lib.ssm_scan_fwd_varlen_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
+    lib.ssm_scan_fwd_varlen_workspace_bytes.restype = SZ
     lib.ssm_state_update.argtypes = [P, P, P, P, I, P, P, P, P, P, P, I64, I64, I64, I, P]
     lib.ssm_state_update.restype = I
     lib.ssm_last_error.argtypes = []
@@ -138,6 +144,67 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
                           _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(out), _ptr(last_state),
                           _ptr(initial_state), batch, L, dim, N, _DTYPES[dt], _ptr(workspace),
                           ws_bytes, ctypes.c_void_p(stream))
+    if rc != 0:
+        _raise(rc)
+    if last_state is not None:
+        return out, last_state
+    return out
+
+
+def ssm_scan_fwd_varlen_workspace_bytes(nseq, total_len, dim, dstate, dtype=torch.bfloat16):
+    return int(load_library().ssm_scan_fwd_varlen_workspace_bytes(nseq, total_len, dim, dstate,
+                                                                  _DTYPES[dtype]))
+
+
+def ssm_scan_fwd_varlen(x, delta, A, B, C, cu_seqlens, D=None, z=None, delta_bias=None,
+                        delta_softplus=True, initial_state=None, return_last_state=False, out=None,
+                        last_state=None, workspace=None, stream=None):
+    """Selective scan forward over packed sequences: x (total_len, dim),
+    B/C (total_len, dstate), cu_seqlens (nseq + 1) int32 offsets on the
+    device; states are (nseq, dim, dstate).
+
+    Returns ``out``, or ``(out, last_state)`` as ``ssm_scan_fwd`` does.
+    """
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be (total_len, dim)")
+    T, dim = x.shape
+    if A.dim() != 2:
+        raise ValueError("A must be (dim, dstate)")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be (nseq + 1,) with nseq >= 1")
+    nseq = cu_seqlens.numel() - 1
+    N = A.shape[1]
+    dev, dt = x.device, x.dtype
+    if dt not in _DTYPES:
+        raise TypeError("activations must be float32 or bfloat16, got %s" % dt)
+    _check(x, "x", (T, dim), dt, dev)
+    _check(delta, "delta", (T, dim), dt, dev)
+    _check(z, "z", (T, dim), dt, dev, optional=True)
+    _check(B, "B", (T, N), dt, dev)
+    _check(C, "C", (T, N), dt, dev)
+    _check(cu_seqlens, "cu_seqlens", (nseq + 1,), torch.int32, dev)
+    _check(A, "A", (dim, N), torch.float32, dev)
+    _check(D, "D", (dim,), torch.float32, dev, optional=True)
+    _check(delta_bias, "delta_bias", (dim,), torch.float32, dev, optional=True)
+    _check(initial_state, "initial_state", (nseq, dim, N), torch.float32, dev, optional=True)
+    if out is None:
+        out = torch.empty((T, dim), dtype=dt, device=dev)
+    _check(out, "out", (T, dim), dt, dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((nseq, dim, N), dtype=torch.float32, device=dev)
+    _check(last_state, "last_state", (nseq, dim, N), torch.float32, dev, optional=True)
+    need = int(lib.ssm_scan_fwd_varlen_workspace_bytes(nseq, T, dim, N, _DTYPES[dt]))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssm_scan_fwd_varlen(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                                 _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(out),
+                                 _ptr(last_state), _ptr(initial_state), _ptr(cu_seqlens), nseq, T,
+                                 dim, N, _DTYPES[dt], _ptr(workspace), ws_bytes,
+                                 ctypes.c_void_p(stream))
     if rc != 0:
         _raise(rc)
     if last_state is not None:

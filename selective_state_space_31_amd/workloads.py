@@ -40,6 +40,16 @@ CONFIGS = {
                         last_state=True, dt_range=(1e-3, 1e-1), steps=1024),
 }
 
+# Packed variable-length prefill: the 130M-shaped layer's 8192 tokens as a
+# batch of prompts of mixed lengths (log-uniform in [64, 4096], drawn from
+# ``seed``) concatenated without padding; fresh prompts (zero initial state),
+# every prompt's final state kept for decoding.
+VARLEN_CONFIGS = {
+    "varlen_mamba130m_bf16": dict(total=8192, len_range=(64, 4096), dim=1536, dstate=16,
+                                  dtype="bf16", gate=True, last_state=True,
+                                  dt_range=(1e-3, 1e-1)),
+}
+
 TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16}
 
 
@@ -206,3 +216,77 @@ def make_decode_tokens(steps, batch, dim, dstate, seed=0, device="cuda", engine=
     bias = torch.from_numpy(_bias_from_dt(dt).astype(np.float32)).to(device)
     return dict(state0=state0, x=x, delta=delta, z=z, B=B, C=C, A=A,
                 D=torch.ones(dim, dtype=torch.float32, device=device), delta_bias=bias)
+
+
+def varlen_lengths(total, len_range, seed=0):
+    """Sequence lengths, log-uniform in ``len_range``, drawn until they
+    cover ``total`` tokens; the last one is cut so they sum to ``total``."""
+    lo, hi = len_range
+    rng = np.random.default_rng(seed + 104729)
+    lens = []
+    while sum(lens) < total:
+        lens.append(int(round(math.exp(rng.uniform(math.log(lo), math.log(hi))))))
+    lens[-1] -= sum(lens) - total
+    return lens
+
+
+class VarlenProblem:
+    """Inputs of one packed-sequence scan call: (total, dim) activations,
+    (total, dstate) B/C, offsets ``cu_seqlens`` (nseq + 1, int32) and
+    per-sequence initial states (nseq, dim, dstate) or None."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+    def tensors(self):
+        return dict(x=self.x, delta=self.delta, A=self.A, B=self.B, C=self.C, D=self.D,
+                    z=self.z, delta_bias=self.delta_bias, initial_state=self.h0,
+                    cu_seqlens=self.cu_seqlens)
+
+    def host_f32(self, s, d_idx=None):
+        """float32 host copies of sequence s alone as a (1, len, .) problem
+        (optionally restricted to channels d_idx), for the oracle."""
+        t0, t1 = self.offsets[s], self.offsets[s + 1]
+
+        def sel(t, cols):
+            if t is None:
+                return None
+            if cols and d_idx is not None:
+                t = t[..., d_idx]
+            return t.to(torch.float32).cpu().numpy()
+        tok = lambda t: None if t is None else t[t0:t1][None]
+        h0 = None if self.h0 is None else self.h0[s:s + 1]
+        if h0 is not None and d_idx is not None:
+            h0 = h0[:, d_idx]
+        return dict(x=sel(tok(self.x), True), delta=sel(tok(self.delta), True),
+                    z=sel(tok(self.z), True), B=sel(tok(self.B), False), C=sel(tok(self.C), False),
+                    A=sel(self.A if d_idx is None else self.A[d_idx], False),
+                    D=sel(None if self.D is None else (self.D if d_idx is None else self.D[d_idx]), False),
+                    delta_bias=sel(None if self.delta_bias is None else
+                                   (self.delta_bias if d_idx is None else self.delta_bias[d_idx]), False),
+                    h0=sel(h0, False))
+
+
+def make_varlen_problem(lengths, dim, dstate, dtype="fp32", gate=True, dt_range=(1e-3, 1e-1),
+                        seed=0, device="cpu", engine="numpy", initial_state=False, **kw):
+    """Packed sequences of the given lengths (zeros allowed): the tokens are
+    drawn as one (1, total, .) problem by ``make_problem`` (same recipe),
+    the initial states from a second seeded stream."""
+    lengths = [int(n) for n in lengths]
+    total = sum(lengths)
+    p = make_problem(1, total, dim, dstate, dtype=dtype, gate=gate, dt_range=dt_range, seed=seed,
+                     device=device, engine=engine, initial_state=False, **kw)
+    nseq = len(lengths)
+    h0 = None
+    if initial_state:
+        rng = np.random.default_rng(seed + 15485863)
+        h0 = torch.from_numpy(rng.standard_normal((nseq, dim, dstate), dtype=np.float32)).to(device)
+    offsets = [0]
+    for n in lengths:
+        offsets.append(offsets[-1] + n)
+    cu = torch.tensor(offsets, dtype=torch.int32, device=device)
+    sq = lambda t: None if t is None else t[0]
+    return VarlenProblem(lengths=lengths, offsets=offsets, nseq=nseq, total=total, dim=dim,
+                         dstate=dstate, dtype=dtype, delta_softplus=p.delta_softplus,
+                         x=sq(p.x), delta=sq(p.delta), z=sq(p.z), B=sq(p.B), C=sq(p.C), A=p.A,
+                         D=p.D, delta_bias=p.delta_bias, h0=h0, cu_seqlens=cu)

@@ -386,3 +386,105 @@ def test_pins_catch_planted_mistakes(name, tmp_path):
 
 def test_unmutated_build_passes_the_same_pins():
     assert _pins_pass(None) is True
+
+
+# ----------------------------------------------------------------------------
+# packed variable-length sequences ("Linear Attention vs Softmax Attention",
+# "Common Mistakes" and "Best Practices" item 4; "State Reset and Isolation")
+# ----------------------------------------------------------------------------
+def _packed_case(rng, lengths, dim, N, h0=True):
+    T = sum(lengths)
+    c = rand_case(rng, 1, T, dim, N, h0=False)
+    flat = {k: (v[0] if isinstance(v, np.ndarray) and v.ndim == 3 and v.shape[:2] == (1, T) else v)
+            for k, v in c.items()}
+    flat["cu"] = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    flat["h0"] = rng.standard_normal((len(lengths), dim, N)).astype(np.float32) if h0 else None
+    return flat
+
+
+def _run_packed(f, fn=None):
+    fn = fn or oracle.scan_varlen
+    return fn(f["x"], f["delta"], f["A"], f["B"], f["C"], f["cu"], D=f["D"], z=f["z"],
+              delta_bias=f["delta_bias"], delta_softplus=f["delta_softplus"], h0=f["h0"])
+
+
+def _packed_vs_brute_force(f, fn=None):
+    """Each packed sequence against the brute-force unrolled sum over its own
+    tokens from its own initial state."""
+    out, last = _run_packed(f, fn)
+    cu = f["cu"]
+    for s in range(len(cu) - 1):
+        t0, t1 = int(cu[s]), int(cu[s + 1])
+        sub = dict(x=f["x"][None, t0:t1], delta=f["delta"][None, t0:t1], A=f["A"],
+                   B=f["B"][None, t0:t1], C=f["C"][None, t0:t1], D=f["D"],
+                   z=None if f["z"] is None else f["z"][None, t0:t1], delta_bias=f["delta_bias"],
+                   h0=None if f["h0"] is None else f["h0"][s:s + 1],
+                   delta_softplus=f["delta_softplus"])
+        if t1 > t0:
+            ref_out, ref_last = brute_force(sub)
+            np.testing.assert_allclose(out[t0:t1], ref_out[0], rtol=1e-11, atol=1e-12)
+        else:
+            ref_last = np.zeros((1,) + last.shape[1:]) if f["h0"] is None else f["h0"][s:s + 1]
+        np.testing.assert_allclose(last[s], ref_last[0], rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("lengths,h0", [
+    ([5, 0, 9, 1, 7], True), ([12], True), ([0, 0, 6], False), ([3, 4, 0], True),
+])
+def test_packed_sequences_equal_brute_force_per_sequence(lengths, h0):
+    rng = np.random.default_rng(sum(lengths) + len(lengths))
+    _packed_vs_brute_force(_packed_case(rng, lengths, 2, 3, h0=h0))
+
+
+def test_packed_differs_from_one_long_sequence():
+    """The reset matters: scanning the concatenation as one sequence (what
+    right-padding-free concatenation without offsets would do) gives a
+    different second sequence."""
+    rng = np.random.default_rng(77)
+    f = _packed_case(rng, [10, 10], 2, 3, h0=False)
+    out, _ = _run_packed(f)
+    one, _ = oracle.scan(f["x"][None], f["delta"][None], f["A"], f["B"][None], f["C"][None],
+                         D=f["D"], z=f["z"][None], delta_bias=f["delta_bias"],
+                         delta_softplus=f["delta_softplus"])
+    np.testing.assert_allclose(out[:10], one[0, :10], rtol=0, atol=0)
+    assert np.abs(out[10:] - one[0, 10:]).max() > 1e-3
+
+
+def _carry_across(x, delta, A, B, C, cu, D=None, z=None, delta_bias=None, delta_softplus=True,
+                  h0=None):
+    # planted mistake: the state runs on into the next sequence (no reset)
+    cu = [int(v) for v in cu]
+    out = np.empty(x.shape)
+    last = np.empty((len(cu) - 1, x.shape[1], A.shape[1]))
+    h = None if h0 is None else h0[0:1]
+    for s in range(len(cu) - 1):
+        sl = slice(cu[s], cu[s + 1])
+        o, l = oracle.scan(x[None, sl], delta[None, sl], A, B[None, sl], C[None, sl], D=D,
+                           z=None if z is None else z[None, sl], delta_bias=delta_bias,
+                           delta_softplus=delta_softplus, h0=h)
+        out[sl] = o[0]
+        last[s] = l[0]
+        h = l.astype(np.float32)
+    return out, last
+
+
+def _shifted_offsets(x, delta, A, B, C, cu, **kw):
+    # planted mistake: every boundary one token late
+    cu = np.asarray(cu).copy()
+    cu[1:-1] += 1
+    return oracle.scan_varlen(x, delta, A, B, C, cu, **kw)
+
+
+def _shared_initial_state(x, delta, A, B, C, cu, h0=None, **kw):
+    # planted mistake: every sequence starts from sequence 0's initial state
+    h = None if h0 is None else np.repeat(h0[0:1], len(cu) - 1, axis=0)
+    return oracle.scan_varlen(x, delta, A, B, C, cu, h0=h, **kw)
+
+
+@pytest.mark.parametrize("mutant", [_carry_across, _shifted_offsets, _shared_initial_state],
+                         ids=lambda f: f.__name__.strip("_"))
+def test_packed_pin_catches_planted_mistakes(mutant):
+    rng = np.random.default_rng(5)
+    f = _packed_case(rng, [6, 5, 7], 2, 3, h0=True)
+    with pytest.raises(AssertionError):
+        _packed_vs_brute_force(f, mutant)

@@ -116,3 +116,19 @@ def test_empty_sequence_copies_initial_state():
     torch.cuda.synchronize()
     assert out.shape == (2, 0, 64)
     assert torch.equal(last, p.h0)
+
+
+def test_resume_in_place_over_chunks():
+    """last_state may be the initial_state buffer; with the sequence cut into
+    many chunks, the output pass must not read initial_state after another
+    chunk has overwritten it."""
+    p = make_problem(2, 4096, 64, 16, dtype="fp32", seed=9, device=DEV, initial_state=True)
+    ref, ref_last = oracle_for(p)
+    buf = p.h0.clone()
+    t = p.tensors()
+    t["initial_state"] = buf
+    out, last = ssm_scan_fwd(**t, last_state=buf)
+    torch.cuda.synchronize()
+    assert last.data_ptr() == buf.data_ptr()
+    assert_close(to_np(out), ref, *TOL["fp32"], what="in place out")
+    assert_close(to_np(last), ref_last, *TOL["fp32"], what="in place last_state")
