@@ -11,8 +11,9 @@ steady-state steps stream from HBM rather than the last-level cache.
 
 Prints ONE JSON line (the metric named on the config) with the roofline of
 the forward kernel and the float64 oracle timed on the host as a baseline,
-plus secondary lines-in-one for the other workloads (2.8B-shaped layer,
-131k-token long context, one decode step).
+plus secondary records for the other workloads (2.8B-shaped layer,
+131k-token long context, the 130M-shaped layer with a general A, the same
+tokens as packed prompts of mixed lengths, one decode step).
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
                   [--no-secondary]
@@ -110,6 +111,41 @@ def fwd_case(name, steps, warmup, replicas, torch, ops, W, seed=0):
     res = dict(workload=name, batch=c["batch"], seq_len=c["L"], dim=c["dim"], dstate=c["dstate"],
                dtype=c["dtype"], gate=c["gate"], last_state=c["last_state"], input_replicas=R,
                ms_per_step=ms, kernel_ms_avg=kern_ms, kernel_ms_median=per[len(per) // 2],
+               tokens_channels_per_s=toks / (ms * 1e-3), algorithmic_bytes=alg,
+               achieved_GBps=alg / (kern_ms * 1e-3) / 1e9)
+    res["pct_of_hbm_peak"] = 100.0 * res["achieved_GBps"] / HBM_PEAK_GBPS
+    del probs, outs, lasts
+    torch.cuda.empty_cache()
+    return res
+
+
+def varlen_case(name, steps, warmup, torch, ops, W, seed=0):
+    """Packed variable-length prefill: the 130M-shaped layer's 8192 tokens as
+    prompts of mixed lengths in one ssm_scan_fwd_varlen call (per-sequence
+    final states written).  Replicas as in fwd_case."""
+    c = dict(W.VARLEN_CONFIGS[name])
+    dev = torch.device("cuda:0")
+    lengths = W.varlen_lengths(c["total"], c["len_range"], seed=seed)
+    nseq = len(lengths)
+    alg = (W.algorithmic_bytes(1, c["total"], c["dim"], c["dstate"], c["dtype"], c["gate"], False)
+           + nseq * c["dim"] * c["dstate"] * 4 + (nseq + 1) * 4)
+    R = max(1, min(8, -(-4 * MALL_BYTES // alg)))
+    probs = [W.make_varlen_problem(lengths, c["dim"], c["dstate"], dtype=c["dtype"], gate=c["gate"],
+                                   dt_range=c["dt_range"], seed=seed + r, device=dev,
+                                   engine="torch_cuda") for r in range(R)]
+    outs = [torch.empty_like(p.x) for p in probs]
+    lasts = [torch.empty(nseq, c["dim"], c["dstate"], device=dev) for _ in probs]
+
+    def call(p, o, l):
+        ops.ssm_scan_fwd_varlen(**p.tensors(), out=o, last_state=l)
+
+    total_ms, per = time_launches(call, list(zip(probs, outs, lasts)), warmup, steps, torch)
+    ms = total_ms / steps
+    kern_ms = sum(per) / len(per)
+    toks = c["total"] * c["dim"]
+    res = dict(workload=name, total_tokens=c["total"], nseq=nseq, lengths=lengths, dim=c["dim"],
+               dstate=c["dstate"], dtype=c["dtype"], gate=c["gate"], last_state=True,
+               input_replicas=R, ms_per_step=ms, kernel_ms_avg=kern_ms,
                tokens_channels_per_s=toks / (ms * 1e-3), algorithmic_bytes=alg,
                achieved_GBps=alg / (kern_ms * 1e-3) / 1e9)
     res["pct_of_hbm_peak"] = 100.0 * res["achieved_GBps"] / HBM_PEAK_GBPS
@@ -222,6 +258,8 @@ def main():
             return
         if a.only == "decode_fp32":
             print(json.dumps(decode_case(a.steps, a.warmup, torch, ops, W)))
+        elif a.only in W.VARLEN_CONFIGS:
+            print(json.dumps(varlen_case(a.only, a.steps, a.warmup, torch, ops, W)))
         else:
             print(json.dumps(fwd_case(a.only, a.steps, a.warmup, a.replicas, torch, ops, W)))
         return
@@ -246,6 +284,8 @@ def main():
             achieved_GBps=main_res["algorithmic_bytes"] / (kms * 1e-3) / 1e9)
         del probs, outs
         torch.cuda.empty_cache()
+        secondary["varlen_mamba130m_bf16"] = varlen_case("varlen_mamba130m_bf16", max(10, a.steps // 2),
+                                                         5, torch, ops, W)
         secondary["decode_fp32"] = decode_case(max(20, a.steps), 5, torch, ops, W)
 
     kern_ms = main_res["kernel_ms_avg"]

@@ -217,10 +217,22 @@ struct FwdArgs {
 constexpr int kGroup = 4;  // tokens per group; the next group's loads are in flight
 constexpr uint32_t kOutOfRange = 0x80000000u;  // > any descriptor's byte range (those are < 2^31)
 
-// Per-lane channel constants.
+// Per-lane channel constants.  The exponents A[d,n]*log2(e) of the general
+// path live in LDS, not in registers: that path is bound by its N
+// transcendentals per token, so reading them back costs little, while
+// holding N more values per lane would cut the resident waves of the whole
+// kernel (the power path needs only A[d,0]).  Table layout: float4 q of
+// lane l at [q][l], so each per-token read is one contiguous 1 KiB row.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <int NT>
+__device__ __forceinline__ f32x4* a2_table() {
+  __shared__ f32x4 tab[NT / 4 * 64];
+  return tab;
+}
+
 template <int NT>
 struct Chan {
-  float A2[NT];  // A[d,n] * log2(e)
+  float A2_0;    // A[d,0] * log2(e)
   float A0;      // A[d,0]
   float bias, dsk;
   int d0;        // first channel of the wave
@@ -238,13 +250,22 @@ __device__ __forceinline__ Chan<NT> load_chan(const FwdArgs<TA>& a, int d0) {
   c.d0 = d0;
   c.valid = d < a.dim;
   const int dl = c.valid ? d : a.dim - 1;  // masked lanes compute on a valid channel
+  static_assert(NT % 4 == 0, "state widths are padded to multiples of 4");
   bool pow_ok = true;
   c.A0 = a.A[static_cast<size_t>(dl) * N];
+  c.A2_0 = c.A0 * kLog2e;
+  f32x4* tab = a2_table<NT>();
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const float an = (EXACT || n < N) ? a.A[static_cast<size_t>(dl) * N + n] : 0.0f;
-    c.A2[n] = an * kLog2e;
-    if (EXACT || n < N) pow_ok = pow_ok && (an == static_cast<float>(n + 1) * c.A0);
+  for (int q = 0; q < NT / 4; ++q) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = 4 * q + j;
+      const float an = (EXACT || n < N) ? a.A[static_cast<size_t>(dl) * N + n] : 0.0f;
+      v[j] = an * kLog2e;
+      if (EXACT || n < N) pow_ok = pow_ok && (an == static_cast<float>(n + 1) * c.A0);
+    }
+    tab[q * 64 + lane] = f32x4{v[0], v[1], v[2], v[3]};
   }
   c.pow = __all(pow_ok);
   c.bias = a.bias ? a.bias[dl] : 0.0f;
@@ -286,7 +307,7 @@ __device__ __forceinline__ StepScalars step_begin(const Chan<NT>& ch, float xv, 
     s.rh = exp_acc(s.dt * ch.A0, s.rl);
     s.p = s.rh;
   } else if constexpr (POW) {
-    s.rh = __builtin_amdgcn_exp2f(s.dt * ch.A2[0]);
+    s.rh = __builtin_amdgcn_exp2f(s.dt * ch.A2_0);
     s.p = s.rh;
   }
   return s;
@@ -296,22 +317,39 @@ __device__ __forceinline__ StepScalars step_begin(const Chan<NT>& ch, float xv, 
 template <int NT, int NB, bool POW, bool ACC, bool AGG>
 __device__ __forceinline__ void step_block(float (&h)[NT], const Chan<NT>& ch, StepScalars& s,
                                            int n0, const float (&Bv)[NB], const float (&Cv)[NB]) {
+  static_assert(NB % 4 == 0, "");
+  if constexpr (POW) {
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int n = n0 + j;
-    float dA;
-    if constexpr (POW) {
-      dA = s.p;
+    for (int j = 0; j < NB; ++j) {
+      const int n = n0 + j;
+      const float dA = s.p;
       if constexpr (ACC) {
         if (n + 1 < NT) s.p = __builtin_fmaf(s.p, s.rh, s.p * s.rl);
       } else {
         s.p *= s.rh;
       }
-    } else {
-      dA = __builtin_amdgcn_exp2f(s.dt * ch.A2[n]);
+      fma_inplace(h[n], dA, s.dx * Bv[j]);
+      if constexpr (!AGG) s.y = __builtin_fmaf(Cv[j], h[n], s.y);
     }
-    fma_inplace(h[n], dA, s.dx * Bv[j]);
-    if constexpr (!AGG) s.y = __builtin_fmaf(Cv[j], h[n], s.y);
+  } else {
+    // Four states at a time, exponents read from the LDS table (volatile:
+    // read per token, never hoisted out of the token loop); the scheduling
+    // barrier keeps the compiler from lifting all N exponentials ahead of
+    // their uses, which would hold N more values per lane.
+    const volatile f32x4* tab = a2_table<NT>();
+#pragma unroll
+    for (int q = 0; q < NB / 4; ++q) {
+      const f32x4 v = tab[(n0 / 4 + q) * 64 + threadIdx.x];
+      const float a2[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + 4 * q + j;
+        const float dA = __builtin_amdgcn_exp2f(s.dt * a2[j]);
+        fma_inplace(h[n], dA, s.dx * Bv[4 * q + j]);
+        if constexpr (!AGG) s.y = __builtin_fmaf(Cv[4 * q + j], h[n], s.y);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -444,10 +482,12 @@ __device__ __forceinline__ void run_tokens(const FwdArgs<TA>& a, const Chan<NT>&
 
   // Main part: pairs of full groups, ping-ponging two register buffers so the
   // loads of the next group are in flight while the current one computes,
-  // and no per-token branch splits the unrolled recurrence.  (Wide states,
-  // N > 16, take the compact token-at-a-time loop below for all tokens.)
+  // and no per-token branch splits the unrolled recurrence.  Wide states
+  // (N > 16) and the general path (bound by its N exponentials per token,
+  // where the buffers would only add register pressure) take the compact
+  // token-at-a-time loop below for all tokens.
   int t_tail = 0;
-  if constexpr (NT <= 16) {
+  if constexpr (NT <= 16 && POW) {
     const int npair = len / (2 * kGroup);
     raw_t xa[kGroup], da[kGroup], za[kGroup], xb2[kGroup], db2[kGroup], zb2[kGroup];
     fetch(0, xa, da, za);
@@ -512,7 +552,7 @@ __device__ __forceinline__ void agg_reverse(const FwdArgs<TA>& a, const Chan<NT>
     const float raw = draw + ch.bias;
     const float dt = SP ? softplus_f32(raw) : raw;
     S += dt;
-    const float r = __builtin_amdgcn_exp2f(dt * ch.A2[0]);
+    const float r = __builtin_amdgcn_exp2f(dt * ch.A2_0);
     float w = dt * xv * Q;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
