@@ -699,8 +699,28 @@ __global__ void __launch_bounds__(64) fwd_scan_kernel(FwdArgs<TA> a) {
         if (EXACT || n < N) lp[n] = h[n];
     }
   } else {
+    // last_state of sequence s (lanes of valid channels)
+    auto store_last = [&](int s, const float (&v)[NT]) {
+      if (a.last_state && ch.valid) {
+        float* lp = a.last_state + (static_cast<size_t>(s) * a.dim + d) * N;
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          if (EXACT || n < N) lp[n] = v[n];
+      }
+    };
+    // empty sequences s, s+1, ... placed at token offset `at`: their last
+    // state is their initial state
+    auto store_empty_from = [&](int s, int at) {
+      if (!a.last_state) return;
+      for (; s < a.nseq && a.cu[s] == at && a.cu[s + 1] == at; ++s) {
+        float e0[NT];
+        load_h0<NT, EXACT>(a.h0, s, a.dim, dl, N, e0);
+        store_last(s, e0);
+      }
+    };
     const int t_end = t_begin + (len > 0 ? len : 0);
     int t = t_begin;
+    if (c == 0) store_empty_from(0, 0);  // empty sequences before the first token
     while (t < t_end) {
       const int s = seq_owner(a.cu, a.nseq, t);
       const int st = a.cu[s], en = a.cu[s + 1];
@@ -711,11 +731,9 @@ __global__ void __launch_bounds__(64) fwd_scan_kernel(FwdArgs<TA> a) {
         run_tokens<TA, NT, EXACT, SP, GATE, true, false>(a, ch, 0, t, e - t, h, S);
       else
         run_tokens<TA, NT, EXACT, SP, GATE, false, false>(a, ch, 0, t, e - t, h, S);
-      if (a.last_state && ch.valid && e == en) {
-        float* lp = a.last_state + (static_cast<size_t>(s) * a.dim + d) * N;
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-          if (EXACT || n < N) lp[n] = h[n];
+      if (e == en) {
+        store_last(s, h);
+        store_empty_from(s + 1, en);  // empty sequences right after this one
       }
       t = e;
     }
@@ -745,8 +763,10 @@ int launch_fwd(const FwdArgs<TA>& a, int64_t batch, hipStream_t s) {
     hipLaunchKernelGGL((fwd_scan_kernel<TA, NT, EXACT, SP, GATE, VL>),
                        dim3(tiles, static_cast<unsigned>(a.K), static_cast<unsigned>(batch)),
                        dim3(64), 0, s, a);
-  // empty packed sequences: last_state = initial state (no token writes it)
-  if (VL && a.last_state) launch_varlen_empty(a.cu, a.nseq, a.h0, a.last_state, a.dim, a.N, s);
+  // no tokens at all: every packed sequence's last_state is its initial state
+  // (otherwise the output pass stores those of the empty ones)
+  if (VL && a.L == 0 && a.last_state)
+    launch_varlen_empty(a.cu, a.nseq, a.h0, a.last_state, a.dim, a.N, s);
   return launch_status(VL ? "ssm_scan_fwd_varlen" : "ssm_scan_fwd");
 }
 

@@ -47,56 +47,162 @@ namespace ssm {
                                                          bool, hipStream_t);
 SSM_FWD_INSTANCES(SSM_EXTERN_FWD)
 
-// Carry pass: one lane per (sequence, state n, channel d), channels fastest.
-// Slot 0 of ws_H receives the initial state; then h runs through the chunk
-// summaries in order, h <- e^(A[d,n] S_c) h + H_c (or h <- H_c where the flag
-// F_c marks a chunk that holds a packed-sequence start), and slot c+1 is
-// overwritten with the state entering chunk c+1.  Summaries are read
-// kCarryBatch chunks at a time, ahead of the stores that overwrite them, so
-// the loads of a batch are in flight together.
-constexpr int kCarryBatch = 32;
-__global__ void __launch_bounds__(256) fwd_carry_kernel(const float* __restrict__ A,
-                                                        const float* __restrict__ h0,
-                                                        const float* __restrict__ ws_S,
-                                                        float* __restrict__ ws_H,
-                                                        const int* __restrict__ ws_F,
-                                                        int64_t batch, int dim, int N, int K) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= batch * N * dim) return;
-  const int d = static_cast<int>(idx % dim);
-  const int n = static_cast<int>((idx / dim) % N);
-  const int64_t b = idx / (static_cast<int64_t>(dim) * N);
-  const float an = A[static_cast<size_t>(d) * N + n];
-  float h = h0 ? h0[(b * dim + d) * N + n] : 0.0f;
-  const size_t sstride = static_cast<size_t>(dim), hstride = static_cast<size_t>(N) * dim;
-  const float* sp = ws_S + static_cast<size_t>(b) * (K - 1) * sstride + d;
-  float* hp = ws_H + (static_cast<size_t>(b) * K * N + n) * dim + d;  // slot 0
-  hp[0] = h;
-  hp += hstride;  // slot c+1 <- chunk c
-  for (int c0 = 0; c0 < K - 1; c0 += kCarryBatch) {
-    const int m = (K - 1 - c0 < kCarryBatch) ? K - 1 - c0 : kCarryBatch;
-    float Sv[kCarryBatch], Hv[kCarryBatch];
-    int Fv[kCarryBatch];
+// Carry pass.  For each (sequence b, state n, channel d) the chunk summaries
+// are folded in order, h <- e^(A[d,n] S_c) h + H_c (or h <- H_c where the
+// flag F_c marks a chunk that holds a packed-sequence start); slot 0 of ws_H
+// receives the initial state and slot c+1 is overwritten with the state
+// entering chunk c+1.
+//
+// The fold is split over the G waves of a workgroup (block = 64 channels of
+// one (b, n), G waves), so that its serial depth is about (K-1)/G and not
+// K-1 even when there are few (b, n, d) lanes:
+//   1. wave g composes the summaries of its range of chunks into one,
+//      (F, S, H) = "forget the incoming state if F, else decay it by
+//      e^(A S); then add H" -- the affine maps compose as (a1,b1) then
+//      (a2,b2) = (a2 a1, a2 b1 + b2), and the decays multiply by adding S;
+//   2. through LDS, wave g folds the composites of waves 0..g-1 onto the
+//      initial state: the state entering its range;
+//   3. wave g walks its range again from there, storing the entering states.
+constexpr int kCarryMaxWaves = 16;
+constexpr int kCarryRegs = 16;  // summaries a wave keeps in registers between steps 1 and 3
+constexpr int kCarryUnroll = 8;
+
+__device__ __forceinline__ float carry_step(float h, float an, float S, float H, int F) {
+  float unused;
+  const float carried = __builtin_fmaf(exp_acc(an * S, unused), h, H);
+  return F ? H : carried;
+}
+
+struct CarryLane {
+  int lane, g, dim, N, K;
+  float an;
+  bool valid;
+  const float* sp;   // ws_S of chunk 0 for this lane
+  const float* hp;   // ws_H slot 1 (chunk 0's summary) for this lane
+  float* hw;         // ws_H slot 1, written
+  size_t sstride, hstride;
+};
+
+// Steps 2 of the fold: the composites of waves 0..g-1 (in LDS) applied to h.
+__device__ __forceinline__ float carry_prefix(const CarryLane& L, float h, const float (*lS)[64],
+                                              const float (*lH)[64], const int* lF) {
+  for (int w = 0; w < L.g; ++w) h = carry_step(h, L.an, lS[w][L.lane], lH[w][L.lane], lF[w]);
+  return h;
+}
+
+__global__ void __launch_bounds__(64 * kCarryMaxWaves) fwd_carry_kernel(
+    const float* __restrict__ A, const float* __restrict__ h0, const float* __restrict__ ws_S,
+    float* __restrict__ ws_H, const int* __restrict__ ws_F, int dim, int N, int K, int per) {
+  __shared__ float lds_S[kCarryMaxWaves][64], lds_H[kCarryMaxWaves][64];
+  __shared__ int lds_F[kCarryMaxWaves];
+  CarryLane L;
+  L.lane = threadIdx.x & 63;
+  L.g = threadIdx.x >> 6;
+  const int n = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int d = blockIdx.x * 64 + L.lane;
+  L.valid = d < dim;
+  const int dl = L.valid ? d : dim - 1;
+  L.an = A[static_cast<size_t>(dl) * N + n];
+  L.sstride = static_cast<size_t>(dim);
+  L.hstride = static_cast<size_t>(N) * dim;
+  L.sp = ws_S + static_cast<size_t>(b) * (K - 1) * L.sstride + dl;
+  float* hslot0 = ws_H + (static_cast<size_t>(b) * K * N + n) * dim + dl;  // slot 0
+  L.hp = hslot0 + L.hstride;  // slot c+1 <- chunk c
+  L.hw = hslot0 + L.hstride;
+  const int c0 = L.g * per;
+  const int c1 = (c0 + per < K - 1) ? c0 + per : K - 1;
+  const float hinit = h0 ? h0[(b * dim + dl) * N + n] : 0.0f;
+  if (L.g == 0 && L.valid) hslot0[0] = hinit;
+
+  if (per <= kCarryRegs) {
+    // the wave's summaries stay in registers from step 1 to step 3
+    float Sv[kCarryRegs], Hv[kCarryRegs];
+    int Fv[kCarryRegs];
 #pragma unroll
-    for (int j = 0; j < kCarryBatch; ++j) {
-      const int jj = j < m ? j : m - 1;
-      Sv[j] = sp[(c0 + jj) * sstride];
-      Hv[j] = hp[(c0 + jj) * hstride];
-      Fv[j] = ws_F ? ws_F[c0 + jj] : 0;
+    for (int j = 0; j < kCarryRegs; ++j) {
+      const int cc = (c0 + j < c1) ? c0 + j : c1 - 1;
+      Sv[j] = L.sp[cc * L.sstride];
+      Hv[j] = L.hp[cc * L.hstride];
+      Fv[j] = ws_F ? ws_F[cc] : 0;
+    }
+    float cS = 0.0f, cH = 0.0f;
+    int cF = 0;
+#pragma unroll
+    for (int j = 0; j < kCarryRegs; ++j) {
+      if (c0 + j < c1) {
+        float unused;
+        const float e = exp_acc(L.an * Sv[j], unused);  // chunk j's decay, kept for step 3
+        cH = Fv[j] ? Hv[j] : __builtin_fmaf(e, cH, Hv[j]);
+        cS = Fv[j] ? Sv[j] : cS + Sv[j];
+        cF |= Fv[j];
+        Sv[j] = e;
+      }
+    }
+    lds_S[L.g][L.lane] = cS;
+    lds_H[L.g][L.lane] = cH;
+    if (L.lane == 0) lds_F[L.g] = cF;
+    __syncthreads();
+    float h = carry_prefix(L, hinit, lds_S, lds_H, lds_F);
+#pragma unroll
+    for (int j = 0; j < kCarryRegs; ++j) {
+      if (c0 + j < c1) {
+        h = Fv[j] ? Hv[j] : __builtin_fmaf(Sv[j], h, Hv[j]);
+        if (L.valid) L.hw[(c0 + j) * L.hstride] = h;
+      }
+    }
+    return;
+  }
+
+  // long ranges: read the summaries twice, kCarryUnroll at a time
+  float cS = 0.0f, cH = 0.0f;
+  int cF = 0;
+  for (int c = c0; c < c1; c += kCarryUnroll) {
+    float Sv[kCarryUnroll], Hv[kCarryUnroll];
+    int Fv[kCarryUnroll];
+#pragma unroll
+    for (int j = 0; j < kCarryUnroll; ++j) {
+      const int cc = (c + j < c1) ? c + j : c1 - 1;
+      Sv[j] = L.sp[cc * L.sstride];
+      Hv[j] = L.hp[cc * L.hstride];
+      Fv[j] = ws_F ? ws_F[cc] : 0;
     }
 #pragma unroll
-    for (int j = 0; j < kCarryBatch; ++j) {
-      if (j < m) {
-        float unused;
-        const float carried = __builtin_fmaf(exp_acc(an * Sv[j], unused), h, Hv[j]);
-        h = Fv[j] ? Hv[j] : carried;
-        hp[(c0 + j) * hstride] = h;
+    for (int j = 0; j < kCarryUnroll; ++j) {
+      if (c + j < c1) {
+        cH = carry_step(cH, L.an, Sv[j], Hv[j], Fv[j]);
+        cS = Fv[j] ? Sv[j] : cS + Sv[j];
+        cF |= Fv[j];
+      }
+    }
+  }
+  lds_S[L.g][L.lane] = cS;
+  lds_H[L.g][L.lane] = cH;
+  if (L.lane == 0) lds_F[L.g] = cF;
+  __syncthreads();
+  float h = carry_prefix(L, hinit, lds_S, lds_H, lds_F);
+  for (int c = c0; c < c1; c += kCarryUnroll) {
+    float Sv[kCarryUnroll], Hv[kCarryUnroll];
+    int Fv[kCarryUnroll];
+#pragma unroll
+    for (int j = 0; j < kCarryUnroll; ++j) {
+      const int cc = (c + j < c1) ? c + j : c1 - 1;
+      Sv[j] = L.sp[cc * L.sstride];
+      Hv[j] = L.hp[cc * L.hstride];
+      Fv[j] = ws_F ? ws_F[cc] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kCarryUnroll; ++j) {
+      if (c + j < c1) {
+        h = carry_step(h, L.an, Sv[j], Hv[j], Fv[j]);
+        if (L.valid) L.hw[(c + j) * L.hstride] = h;
       }
     }
   }
 }
 
 // Packed sequences with no tokens: last_state = initial state (or zeros).
+// Used when the call has no tokens at all (else the output pass stores them).
 // Block (s, part): the blocks of a sequence that has tokens leave at once.
 __global__ void __launch_bounds__(256) fwd_varlen_empty_kernel(const int* __restrict__ cu,
                                                                const float* __restrict__ h0,
@@ -349,11 +455,28 @@ int launch_status(const char* what) {
   return SSM_OK;
 }
 
+int device_cus();
+
+// Waves per carry workgroup: enough in total for a few waves per SIMD, at
+// least kCarryUnroll chunk summaries per wave, and at most kCarryRegs where
+// kCarryMaxWaves waves allow it.
 void launch_carry(const float* A, const float* h0, const float* ws_S, float* ws_H,
                   const int* ws_F, int64_t batch, int dim, int N, int K, hipStream_t s) {
-  const int64_t lanes = batch * N * dim;
-  hipLaunchKernelGGL(fwd_carry_kernel, dim3(static_cast<unsigned>((lanes + 255) / 256)), dim3(256),
-                     0, s, A, h0, ws_S, ws_H, ws_F, batch, dim, N, K);
+  const int64_t blocks = static_cast<int64_t>((dim + 63) / 64) * N * batch;
+  const int64_t target = 4LL * 4 * device_cus();
+  int G = static_cast<int>((target + blocks - 1) / blocks);
+  const int gmax = (K - 1 + kCarryUnroll - 1) / kCarryUnroll;
+  G = G < gmax ? G : gmax;
+  // keep each wave's range within its registers where 16 waves allow it
+  const int gregs = (K - 1 + kCarryRegs - 1) / kCarryRegs;
+  G = G > gregs ? G : gregs;
+  G = G < kCarryMaxWaves ? (G > 1 ? G : 1) : kCarryMaxWaves;
+  const int per = (K - 1 + G - 1) / G;
+  G = (K - 1 + per - 1) / per;
+  hipLaunchKernelGGL(fwd_carry_kernel,
+                     dim3(static_cast<unsigned>((dim + 63) / 64), static_cast<unsigned>(N),
+                          static_cast<unsigned>(batch)),
+                     dim3(64 * G), 0, s, A, h0, ws_S, ws_H, ws_F, dim, N, K, per);
 }
 
 void launch_varlen_empty(const int* cu, int nseq, const float* h0, float* last_state, int dim,
@@ -371,8 +494,12 @@ void launch_varlen_empty(const int* cu, int nseq, const float* h0, float* last_s
 #ifndef SSM_WAVES_PER_SIMD
 #define SSM_WAVES_PER_SIMD 8
 #endif
+#ifndef SSM_MIN_CHUNK
+#define SSM_MIN_CHUNK 32
+#endif
 constexpr int kWavesPerSimd = SSM_WAVES_PER_SIMD;
-constexpr int kMinChunk = 32;
+constexpr int kMinChunk = SSM_MIN_CHUNK;
+static_assert(kMinChunk % (2 * kGroup) == 0, "chunks are whole pairs of token groups");
 
 struct Plan {
   int K;
