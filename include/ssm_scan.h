@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 2
+#define SSM_SCAN_ABI_VERSION 3
 
 typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
 
@@ -158,6 +158,45 @@ int ssm_state_update(float* state, const void* x, const void* delta, const float
                      int delta_softplus, const float* A, const void* B, const void* C,
                      const float* D_skip, const void* z, void* out,
                      int64_t batch, int64_t dim, int64_t dstate, int dtype, hipStream_t stream);
+
+/*
+ * Causal depthwise convolution + SiLU, the step that produces the scan's x.
+ * "Linear Attention vs Softmax Attention: Can RWKV or Mamba Replace
+ * Transformers?" (shyankdev.com), section "Implementation": the main branch
+ * passes through a depthwise Conv1d (kernel_size taps per channel, bias,
+ * padding kernel_size - 1, output cut to seq_len: causal) and then SiLU; the
+ * figure on the same page gives k = 4.  With W = width:
+ *   out[b,t,d] = silu( bias[d] + sum_{k<W} weight[d,k] * xx[b, t-(W-1)+k, d] )
+ * where xx is x with the conv state in front: xx[b,s,d] = x[b,s,d] for s >= 0
+ * and initial_conv_state[b, d, (W-1)+s] for -(W-1) <= s < 0 (zeros if NULL,
+ * the page's zero padding).  Tap W-1 multiplies the current token.
+ *   x, out             : (batch, seqlen, dim) act
+ *   weight             : (dim, width) float32;  bias : (dim) float32 or NULL
+ *   initial_conv_state : (batch, dim, width-1) act or NULL; the inputs
+ *                        before the first token, oldest first
+ *   final_conv_state   : (batch, dim, width-1) act or NULL; receives the last
+ *                        width-1 inputs (exact copies), oldest first
+ *   silu               : 1 = apply SiLU, 0 = the convolution alone
+ *   2 <= width <= 4; batch, dim >= 1; seqlen >= 0.
+ * Arithmetic is float32 (fused multiply-adds in tap order); bf16 outputs are
+ * rounded to nearest even.  Outputs may not overlap inputs.
+ */
+int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
+                          const void* initial_conv_state, void* out, void* final_conv_state,
+                          int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int silu,
+                          int dtype, hipStream_t stream);
+
+/*
+ * One decoding step of the convolution above for `batch` sequences:
+ *   conv_state : (batch, dim, width-1) act, read and shifted in place (the
+ *                oldest input drops out, x becomes the newest)
+ *   x, out     : (batch, dim) act;  weight, bias, silu, width, dtype as above.
+ * Equivalent to ssm_causal_conv1d_fwd with seqlen = 1 and initial_conv_state
+ * = final_conv_state = conv_state.
+ */
+int ssm_causal_conv1d_update(void* conv_state, const void* x, const float* weight,
+                             const float* bias, void* out, int64_t batch, int64_t dim,
+                             int64_t width, int silu, int dtype, hipStream_t stream);
 
 /* Message for the most recent non-OK status returned on the calling thread
  * ("" if none).  The pointer stays valid until the next call on that thread. */

@@ -29,6 +29,7 @@
 
 #include "ssm_scan.h"
 
+#include "host_util.hpp"
 #include "kernels.hpp"
 
 namespace ssm {
@@ -426,7 +427,8 @@ __global__ void __launch_bounds__(256) decode_scalar_kernel(DecArgs<TA> a) {
 // ----------------------------------------------------------------------------
 thread_local char g_err[512] = "";
 
-int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error() { g_err[0] = '\0'; }
+
 int fail(int code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -436,12 +438,6 @@ int fail(int code, const char* fmt, ...) {
 }
 
 bool aligned(const void* p, size_t k) { return (reinterpret_cast<uintptr_t>(p) % k) == 0; }
-
-struct Span {
-  const void* p;
-  size_t bytes;
-  const char* name;
-};
 
 bool overlap(const Span& a, const Span& b) {
   if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
@@ -454,8 +450,6 @@ int launch_status(const char* what) {
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
   return SSM_OK;
 }
-
-int device_cus();
 
 // Waves per carry workgroup: enough in total for a few waves per SIMD, at
 // least kCarryUnroll chunk summaries per wave, and at most kCarryRegs where

@@ -21,8 +21,8 @@ STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL", -2: "SSM_ERR_SHAPE", -3: "SSM_ERR_UNS
           -4: "SSM_ERR_ALIGN", -5: "SSM_ERR_ALIAS", -6: "SSM_ERR_WORKSPACE", -7: "SSM_ERR_HIP"}
 
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd_varlen",
-           "ssm_scan_fwd_varlen_workspace_bytes", "ssm_state_update", "ssm_last_error",
-           "ssm_abi_version")
+           "ssm_scan_fwd_varlen_workspace_bytes", "ssm_state_update", "ssm_causal_conv1d_fwd",
+           "ssm_causal_conv1d_update", "ssm_last_error", "ssm_abi_version")
 
 
 class SsmError(RuntimeError):
@@ -55,6 +55,10 @@ def load_library(path=LIB_PATH):
     lib.ssm_scan_fwd_varlen_workspace_bytes.restype = SZ
     lib.ssm_state_update.argtypes = [P, P, P, P, I, P, P, P, P, P, P, I64, I64, I64, I, P]
     lib.ssm_state_update.restype = I
+    lib.ssm_causal_conv1d_fwd.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I, I, P]
+    lib.ssm_causal_conv1d_fwd.restype = I
+    lib.ssm_causal_conv1d_update.argtypes = [P, P, P, P, P, I64, I64, I64, I, I, P]
+    lib.ssm_causal_conv1d_update.restype = I
     lib.ssm_last_error.argtypes = []
     lib.ssm_last_error.restype = ctypes.c_char_p
     lib.ssm_abi_version.argtypes = []
@@ -241,6 +245,71 @@ def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None,
     rc = lib.ssm_state_update(_ptr(state), _ptr(x), _ptr(delta), _ptr(delta_bias),
                               int(bool(delta_softplus)), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                               _ptr(out), batch, dim, N, _DTYPES[dt], ctypes.c_void_p(stream))
+    if rc != 0:
+        _raise(rc)
+    return out
+
+
+def ssm_causal_conv1d_fwd(x, weight, bias=None, initial_conv_state=None, silu=True,
+                          return_final_state=False, out=None, final_conv_state=None, stream=None):
+    """Causal depthwise convolution (+ SiLU) over (batch, seqlen, dim)
+    activations; weight (dim, width) float32, conv states (batch, dim,
+    width-1) in x's dtype.  Returns ``out``, or ``(out, final_conv_state)``."""
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, seqlen, dim)")
+    batch, L, dim = x.shape
+    if weight.dim() != 2:
+        raise ValueError("weight must be (dim, width)")
+    W = weight.shape[1]
+    dev, dt = x.device, x.dtype
+    if dt not in _DTYPES:
+        raise TypeError("activations must be float32 or bfloat16, got %s" % dt)
+    _check(x, "x", (batch, L, dim), dt, dev)
+    _check(weight, "weight", (dim, W), torch.float32, dev)
+    _check(bias, "bias", (dim,), torch.float32, dev, optional=True)
+    _check(initial_conv_state, "initial_conv_state", (batch, dim, W - 1), dt, dev, optional=True)
+    if out is None:
+        out = torch.empty((batch, L, dim), dtype=dt, device=dev)
+    _check(out, "out", (batch, L, dim), dt, dev)
+    if final_conv_state is None and return_final_state:
+        final_conv_state = torch.empty((batch, dim, W - 1), dtype=dt, device=dev)
+    _check(final_conv_state, "final_conv_state", (batch, dim, W - 1), dt, dev, optional=True)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssm_causal_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(initial_conv_state),
+                                   _ptr(out), _ptr(final_conv_state), batch, L, dim, W,
+                                   int(bool(silu)), _DTYPES[dt], ctypes.c_void_p(stream))
+    if rc != 0:
+        _raise(rc)
+    if final_conv_state is not None:
+        return out, final_conv_state
+    return out
+
+
+def ssm_causal_conv1d_update(conv_state, x, weight, bias=None, silu=True, out=None, stream=None):
+    """One decoding step: ``conv_state`` (batch, dim, width-1) in x's dtype is
+    shifted in place; returns ``out`` (batch, dim)."""
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be (batch, dim)")
+    batch, dim = x.shape
+    W = weight.shape[1]
+    dev, dt = x.device, x.dtype
+    if dt not in _DTYPES:
+        raise TypeError("activations must be float32 or bfloat16, got %s" % dt)
+    _check(conv_state, "conv_state", (batch, dim, W - 1), dt, dev)
+    _check(x, "x", (batch, dim), dt, dev)
+    _check(weight, "weight", (dim, W), torch.float32, dev)
+    _check(bias, "bias", (dim,), torch.float32, dev, optional=True)
+    if out is None:
+        out = torch.empty((batch, dim), dtype=dt, device=dev)
+    _check(out, "out", (batch, dim), dt, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssm_causal_conv1d_update(_ptr(conv_state), _ptr(x), _ptr(weight), _ptr(bias),
+                                      _ptr(out), batch, dim, W, int(bool(silu)), _DTYPES[dt],
+                                      ctypes.c_void_p(stream))
     if rc != 0:
         _raise(rc)
     return out

@@ -40,6 +40,14 @@ CONFIGS = {
                         last_state=True, dt_range=(1e-3, 1e-1), steps=1024),
 }
 
+# The causal depthwise convolution before the scan (width 4, SiLU) on the
+# 130M-shaped layer's activations, and its per-token update at the decode
+# shape.
+CONV_CONFIGS = {
+    "conv1d_mamba130m_bf16": dict(batch=4, L=2048, dim=1536, width=4, dtype="bf16"),
+    "conv1d_decode_fp32": dict(batch=256, L=1, dim=5120, width=4, dtype="fp32"),
+}
+
 # Packed variable-length prefill: the 130M-shaped layer's 8192 tokens as a
 # batch of prompts of mixed lengths (log-uniform in [64, 4096], drawn from
 # ``seed``) concatenated without padding; fresh prompts (zero initial state),
@@ -290,3 +298,35 @@ def make_varlen_problem(lengths, dim, dstate, dtype="fp32", gate=True, dt_range=
                          dstate=dstate, dtype=dtype, delta_softplus=p.delta_softplus,
                          x=sq(p.x), delta=sq(p.delta), z=sq(p.z), B=sq(p.B), C=sq(p.C), A=p.A,
                          D=p.D, delta_bias=p.delta_bias, h0=h0, cu_seqlens=cu)
+
+
+def make_conv_problem(batch, L, dim, width=4, dtype="fp32", seed=0, device="cpu", engine="numpy",
+                      initial_state=False, with_bias=True, **_):
+    """Inputs of the causal depthwise convolution: x ~ N(0,1) (batch, L, dim)
+    in the activation dtype; weight (dim, width) and bias (dim) uniform in
+    +-1/sqrt(width) (PyTorch's default bound for a depthwise Conv1d, fan-in =
+    width), float32; conv state (batch, dim, width-1) ~ N(0,1) in the
+    activation dtype.  Draw order: weight, bias, x, state."""
+    bound = 1.0 / math.sqrt(width)
+    tdt = TORCH_DTYPE[dtype]
+    if engine == "numpy":
+        rng = np.random.default_rng(seed + 271828)
+        w = torch.from_numpy(rng.uniform(-bound, bound, (dim, width)).astype(np.float32))
+        bias = torch.from_numpy(rng.uniform(-bound, bound, dim).astype(np.float32))
+        x = _to_dtype(rng.standard_normal((batch, L, dim), dtype=np.float32), dtype)
+        st = (_to_dtype(rng.standard_normal((batch, dim, width - 1), dtype=np.float32), dtype)
+              if initial_state else None)
+        move = lambda t: None if t is None else t.to(device)
+        w, bias, x, st = map(move, (w, bias, x, st))
+    elif engine == "torch_cuda":
+        g = torch.Generator(device=device)
+        g.manual_seed(seed + 271828)
+        w = torch.empty(dim, width, device=device).uniform_(-bound, bound, generator=g)
+        bias = torch.empty(dim, device=device).uniform_(-bound, bound, generator=g)
+        x = torch.randn(batch, L, dim, generator=g, device=device).to(tdt)
+        st = (torch.randn(batch, dim, width - 1, generator=g, device=device).to(tdt)
+              if initial_state else None)
+    else:
+        raise ValueError(engine)
+    return Problem(batch=batch, L=L, dim=dim, width=width, dtype=dtype, x=x, weight=w,
+                   bias=bias if with_bias else None, state0=st)

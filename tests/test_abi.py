@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -26,8 +26,8 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd_varlen",
-         "ssm_scan_fwd_varlen_workspace_bytes", "ssm_state_update", "ssm_last_error",
-         "ssm_abi_version"])
+         "ssm_scan_fwd_varlen_workspace_bytes", "ssm_state_update", "ssm_causal_conv1d_fwd",
+         "ssm_causal_conv1d_update", "ssm_last_error", "ssm_abi_version"])
 
 
 def test_binding_lists_every_declared_symbol():
@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ssm_abi_version() == 2
+    assert lib.ssm_abi_version() == 3
 
 
 def test_workspace_query_is_host_only(lib):
@@ -133,3 +133,37 @@ def test_fwd_varlen_needs_its_workspace(lib):
     assert need > 0
     assert _fwd_varlen(lib, T=8192, ws=ctypes.c_void_p(0x30000000), wsb=need - 1) == -6
     assert _fwd_varlen(lib, T=8192, ws=ctypes.c_void_p(0x30000000 + 64), wsb=need) == -4
+
+
+def _conv(lib, **kw):
+    """ssm_causal_conv1d_fwd with fake (never dereferenced) pointers."""
+    P = ctypes.c_void_p
+    fake = lambda k: P(0x10000000 + 0x1000000 * k)
+    a = dict(x=fake(1), w=fake(2), bias=None, s0=None, out=fake(3), s1=None, batch=2, L=8,
+             dim=64, W=4, silu=1, dtype=1, stream=None)
+    a.update(kw)
+    return lib.ssm_causal_conv1d_fwd(a["x"], a["w"], a["bias"], a["s0"], a["out"], a["s1"],
+                                     a["batch"], a["L"], a["dim"], a["W"], a["silu"], a["dtype"],
+                                     a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w=None), -1), (dict(x=None), -1), (dict(batch=0), -2), (dict(L=-1), -2),
+    (dict(W=1), -3), (dict(W=5), -3), (dict(silu=2), -3), (dict(dtype=3), -3),
+    (dict(x=ctypes.c_void_p(0x11000001)), -4), (dict(w=ctypes.c_void_p(0x12000002)), -4),
+    (dict(out=ctypes.c_void_p(0x11000000 + 64)), -5),
+    (dict(s1=ctypes.c_void_p(0x13000000 + 32)), -5),
+])
+def test_conv_fwd_rejects_bad_arguments_before_launch(lib, kw, code):
+    assert _conv(lib, **kw) == code
+    assert lib.ssm_last_error()
+
+
+def test_conv_update_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p
+    f = lambda k: P(0x10000000 + 0x1000000 * k)
+    # NULL state, width 5, out overlapping the state
+    assert lib.ssm_causal_conv1d_update(None, f(1), f(2), None, f(3), 2, 64, 4, 1, 1, None) == -1
+    assert lib.ssm_causal_conv1d_update(f(4), f(1), f(2), None, f(3), 2, 64, 5, 1, 1, None) == -3
+    assert lib.ssm_causal_conv1d_update(f(4), f(1), f(2), None, P(0x14000000 + 2), 2, 64, 4, 1, 1,
+                                        None) == -5
