@@ -9,9 +9,10 @@
 // activation once in and once out and does W multiply-adds per value: it is
 // bound by HBM bandwidth, so the kernels are laid out for wide coalesced
 // accesses rather than arithmetic:
-//   * a lane owns V consecutive channels (16 bytes of activations: 8 bf16 or
-//     4 float32) and a stretch of kConvTokens tokens; a wave covers 64*V
-//     channels of one token in one 1 KiB access per token;
+//   * a lane owns V consecutive channels (2 bf16 or 4 float32: 4- or 16-byte
+//     accesses; for bf16 the narrower vector measured faster than 8, as it
+//     gives more waves for the same bytes) and a stretch of kConvTokens
+//     tokens; a wave covers 64*V channels of one token per access;
 //   * the lane loads the W-1 inputs before its stretch itself (from x or the
 //     conv state), so stretches are independent and the launch has enough
 //     waves for the whole chip at any sequence length;
@@ -28,7 +29,10 @@
 
 namespace ssm {
 
-constexpr int kConvTokens = 16;  // tokens per lane in the forward
+#ifndef SSM_CONV_TOKENS
+#define SSM_CONV_TOKENS 16
+#endif
+constexpr int kConvTokens = SSM_CONV_TOKENS;  // tokens per lane in the forward
 
 template <typename TA>
 struct ConvArgs {
@@ -61,30 +65,58 @@ struct VecIo<float, 4> {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   }
 };
-template <>
-struct VecIo<bf16_t, 8> {
-  using raw_t = uint4;
-  __device__ static raw_t load(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+// bf16: V = 2, 4 or 8 values in one 4-, 8- or 16-byte access.
+template <int V>
+struct VecBf16 {
+  static constexpr int NW = V / 2;  // 32-bit words
+  struct raw_t {
+    uint32_t w[NW];
+  };
+  __device__ static raw_t load(const bf16_t* p) {
+    raw_t r;
+    if constexpr (NW == 4) {
+      const uint4 q = *reinterpret_cast<const uint4*>(p);
+      r.w[0] = q.x; r.w[1] = q.y; r.w[2] = q.z; r.w[3] = q.w;
+    } else if constexpr (NW == 2) {
+      const uint2 q = *reinterpret_cast<const uint2*>(p);
+      r.w[0] = q.x; r.w[1] = q.y;
+    } else {
+      r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+    return r;
+  }
   __device__ static float get(const raw_t& r, int v) {
-    const uint32_t w = (v >> 1) == 0 ? r.x : (v >> 1) == 1 ? r.y : (v >> 1) == 2 ? r.z : r.w;
+    const uint32_t w = r.w[v >> 1];
     return __uint_as_float((v & 1) ? (w & 0xffff0000u) : (w << 16));
   }
   __device__ static uint32_t bits(float f) {
     __bf16 b = static_cast<__bf16>(f);  // round to nearest even (exact for bf16 values)
     return __builtin_bit_cast(uint16_t, b);
   }
-  __device__ static raw_t from(const float (&v)[8]) {
-    uint4 q;
-    q.x = bits(v[0]) | (bits(v[1]) << 16);
-    q.y = bits(v[2]) | (bits(v[3]) << 16);
-    q.z = bits(v[4]) | (bits(v[5]) << 16);
-    q.w = bits(v[6]) | (bits(v[7]) << 16);
-    return q;
+  __device__ static raw_t from(const float (&v)[V]) {
+    raw_t r;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) r.w[i] = bits(v[2 * i]) | (bits(v[2 * i + 1]) << 16);
+    return r;
   }
-  __device__ static void store(bf16_t* p, const float (&v)[8]) {
-    *reinterpret_cast<uint4*>(p) = from(v);
+  __device__ static void store(bf16_t* p, const float (&v)[V]) {
+    const raw_t r = from(v);
+    if constexpr (NW == 4) {
+      *reinterpret_cast<uint4*>(p) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+    } else if constexpr (NW == 2) {
+      *reinterpret_cast<uint2*>(p) = make_uint2(r.w[0], r.w[1]);
+    } else {
+      *reinterpret_cast<uint32_t*>(p) = r.w[0];
+    }
   }
 };
+template <>
+struct VecIo<bf16_t, 8> : VecBf16<8> {};
+template <>
+struct VecIo<bf16_t, 4> : VecBf16<4> {};
+template <>
+struct VecIo<bf16_t, 2> : VecBf16<2> {};
+
 template <typename TA>
 struct VecIo1 {
   using raw_t = float;
@@ -105,11 +137,18 @@ __device__ __forceinline__ float conv_input(const ConvArgs<TA>& a, int64_t b, in
   return a.state0 ? to_f32(a.state0[(b * a.dim + c) * (W - 1) + (W - 1) + s]) : 0.0f;
 }
 
-// Block = one wave: (channel tile, token stretch, sequence) from a flat index.
+// Block = one wave: a unit (channel tile, token stretch, sequence), tiles
+// fastest.  Workgroups are dealt to the 8 XCDs in turn (block i to XCD i mod
+// 8), each with its own L2; the units are handed out so that every XCD
+// works through one contiguous range of them, so the W-1 rows a stretch
+// shares with the one before it are found in that XCD's L2.
+constexpr int kXcds = 8;
 template <typename TA, int W, int V, bool SILU>
 __global__ void __launch_bounds__(64) conv_fwd_kernel(ConvArgs<TA> a) {
   constexpr int T = kConvTokens;
-  const int64_t blk = blockIdx.x;
+  const int64_t per_xcd = gridDim.x / kXcds;  // the grid is a multiple of kXcds
+  const int64_t blk = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (blk >= static_cast<int64_t>(a.tiles) * a.chunks * a.batch) return;
   const int tile = static_cast<int>(blk % a.tiles);
   const int64_t rest = blk / a.tiles;
   const int64_t t0 = (rest % a.chunks) * T;
@@ -118,19 +157,27 @@ __global__ void __launch_bounds__(64) conv_fwd_kernel(ConvArgs<TA> a) {
   if (c0 >= a.dim) return;  // (no barriers below)
   const int64_t L = a.L;
 
-  // inputs t0-(W-1) .. t0+T-1 (raw), all loads issued up front
+  // inputs t0-(W-1) .. t0+T-1 (raw), all loads issued up front.  Interior
+  // stretches (every row inside the sequence; the common case, uniform per
+  // wave) load without a branch per row, so the loads are in flight together.
   using IO = VecIo<TA, V>;
   typename IO::raw_t win[T + W - 1];
+  const TA* xrow = a.x + (b * L + t0 - (W - 1)) * a.dim + c0;
+  if (t0 >= W - 1 && t0 + T <= L) {
 #pragma unroll
-  for (int r = 0; r < T + W - 1; ++r) {
-    const int64_t t = t0 - (W - 1) + r;
-    if (t >= 0 && t < L) {
-      win[r] = IO::load(a.x + (b * L + t) * a.dim + c0);
-    } else {
-      float v0[V];
+    for (int r = 0; r < T + W - 1; ++r) win[r] = IO::load(xrow + static_cast<int64_t>(r) * a.dim);
+  } else {
 #pragma unroll
-      for (int v = 0; v < V; ++v) v0[v] = (t < 0) ? conv_input<TA, W>(a, b, t, c0 + v) : 0.0f;
-      win[r] = IO::from(v0);
+    for (int r = 0; r < T + W - 1; ++r) {
+      const int64_t t = t0 - (W - 1) + r;
+      if (t >= 0 && t < L) {
+        win[r] = IO::load(a.x + (b * L + t) * a.dim + c0);
+      } else {
+        float v0[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) v0[v] = (t < 0) ? conv_input<TA, W>(a, b, t, c0 + v) : 0.0f;
+        win[r] = IO::from(v0);
+      }
     }
   }
   float wt[V][W], bs[V];
@@ -140,10 +187,11 @@ __global__ void __launch_bounds__(64) conv_fwd_kernel(ConvArgs<TA> a) {
     for (int k = 0; k < W; ++k) wt[v][k] = a.w[static_cast<size_t>(c0 + v) * W + k];
     bs[v] = a.bias ? a.bias[c0 + v] : 0.0f;
   }
+  const int jend = (L - t0 < T) ? static_cast<int>(L - t0) : T;  // outputs in this stretch
 #pragma unroll
   for (int j = 0; j < T; ++j) {
     const int64_t t = t0 + j;
-    if (t < L) {
+    if (j < jend) {
       float o[V];
 #pragma unroll
       for (int v = 0; v < V; ++v) {
@@ -208,7 +256,8 @@ int launch_conv_fwd(const ConvArgs<TA>& a0, int W, bool silu, hipStream_t s) {
   ConvArgs<TA> a = a0;
   a.tiles = (a.dim + 64 * V - 1) / (64 * V);
   a.chunks = a.L > 0 ? (a.L + kConvTokens - 1) / kConvTokens : 1;
-  const int64_t blocks = static_cast<int64_t>(a.tiles) * a.chunks * a.batch;
+  const int64_t units = static_cast<int64_t>(a.tiles) * a.chunks * a.batch;
+  const int64_t blocks = (units + kXcds - 1) / kXcds * kXcds;
   const dim3 grid(static_cast<unsigned>(blocks)), block(64);
 #define SSM_CONV_CASE(WW)                                                               \
   case WW:                                                                              \
@@ -294,12 +343,15 @@ int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
         return fail(SSM_ERR_ALIAS, "%s: output %s overlaps input %s", fn, o.name, i.name);
   if (overlap(outs[0], outs[1])) return fail(SSM_ERR_ALIAS, "%s: out overlaps final_conv_state", fn);
   if (seqlen == 0 && !final_conv_state) return SSM_OK;
-  // 16-byte vectors of channels where the layout allows them
-  const int V = dtype == SSM_DTYPE_F32 ? 4 : 8;
-  const bool vec = dim % V == 0 && (seqlen == 0 || (aligned(x, 16) && aligned(out, 16)));
+  // vectors of channels where the layout allows them (bf16: 2, 4 or 8)
+#ifndef SSM_CONV_VEC_BF16
+#define SSM_CONV_VEC_BF16 2
+#endif
+  const int V = dtype == SSM_DTYPE_F32 ? 4 : SSM_CONV_VEC_BF16;
+  const bool vec = dim % V == 0 && (seqlen == 0 || (aligned(x, V * es) && aligned(out, V * es)));
   const int64_t tiles = (dim + 64 * (vec ? V : 1) - 1) / (64 * (vec ? V : 1));
   const int64_t chunks = seqlen > 0 ? (seqlen + kConvTokens - 1) / kConvTokens : 1;
-  if (tiles * chunks * batch > kConvMaxBlocks)
+  if (tiles * chunks * batch + kXcds > kConvMaxBlocks)
     return fail(SSM_ERR_SHAPE, "%s: problem too large for one launch", fn);
   const bool sl = silu != 0;
   if (dtype == SSM_DTYPE_F32) {
@@ -314,7 +366,7 @@ int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
                      static_cast<const bf16_t*>(initial_conv_state), static_cast<bf16_t*>(out),
                      static_cast<bf16_t*>(final_conv_state), batch, seqlen, static_cast<int>(dim),
                      0, 0};
-  return vec ? launch_conv_fwd<bf16_t, 8>(a, static_cast<int>(width), sl, stream)
+  return vec ? launch_conv_fwd<bf16_t, SSM_CONV_VEC_BF16>(a, static_cast<int>(width), sl, stream)
              : launch_conv_fwd<bf16_t, 1>(a, static_cast<int>(width), sl, stream);
 }
 

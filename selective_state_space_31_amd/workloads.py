@@ -41,10 +41,11 @@ CONFIGS = {
 }
 
 # The causal depthwise convolution before the scan (width 4, SiLU) on the
-# 130M-shaped layer's activations, and its per-token update at the decode
-# shape.
+# 130M- and 2.8B-shaped layers' activations, and its per-token update at the
+# decode shape.
 CONV_CONFIGS = {
     "conv1d_mamba130m_bf16": dict(batch=4, L=2048, dim=1536, width=4, dtype="bf16"),
+    "conv1d_mamba2p8b_bf16": dict(batch=8, L=4096, dim=5120, width=4, dtype="bf16"),
     "conv1d_decode_fp32": dict(batch=256, L=1, dim=5120, width=4, dtype="fp32"),
 }
 
