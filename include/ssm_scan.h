@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 3
+#define SSM_SCAN_ABI_VERSION 4
 
 typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
 
@@ -144,6 +144,49 @@ int ssm_scan_fwd_varlen(const void* x, const void* delta, const float* delta_bia
  * invalid sizes). */
 size_t ssm_scan_fwd_varlen_workspace_bytes(int64_t nseq, int64_t total_len, int64_t dim,
                                            int64_t dstate, int dtype);
+
+/*
+ * Gradients of ssm_scan_fwd (the backward pass used in training).  The
+ * pages give the forward only; the gradients are those of its loop, for the
+ * scalar loss = sum(dout * out) + sum(dlast_state * last_state), with
+ * respect to every input.  Like the forward, it keeps no per-token states
+ * in memory but recomputes them stripe by stripe, the memory trick that the
+ * chenyuan1125.github.io page on Mamba's selective state spaces (section
+ * "Selectivity Removes the Convolution Shortcut; Scan Restores
+ * Parallelism") attributes to the original kernel's backward pass.
+ *   inputs: as ssm_scan_fwd (x, delta, delta_bias, delta_softplus, A, B, C,
+ *           D_skip, z, initial_state; same layouts and dtypes), plus
+ *     dout         : (batch, seqlen, dim) act, the gradient of out
+ *     dlast_state  : (batch, dim, dstate) float32 or NULL (= 0)
+ *   outputs (all overwritten, none accumulated into):
+ *     dx, ddelta   : (batch, seqlen, dim) act; ddelta is the gradient of
+ *                    the raw delta (before bias and softplus)
+ *     dz           : (batch, seqlen, dim) act; required when z is given
+ *     dA           : (dim, dstate) float32
+ *     dB, dC       : (batch, seqlen, dstate) float32
+ *     dD           : (dim) float32 or NULL (must be NULL without D_skip)
+ *     ddelta_bias  : (dim) float32 or NULL
+ *     dinitial_state : (batch, dim, dstate) float32 or NULL
+ *   dstate must be 4, 8 or 16 (SSM_ERR_UNSUPPORTED otherwise); alignment as
+ *   ssm_scan_fwd, with B and C aligned to 4 elements and dB, dC to 16 bytes.
+ *   workspace: at least ssm_scan_bwd_workspace_bytes(...) bytes, 256-byte
+ *   aligned (0 when seqlen is 0).
+ * Arithmetic is float32; the sums over channels, tokens and sequences are
+ * formed from per-workgroup partials added in a fixed order, so results are
+ * bitwise reproducible run to run on one device.  Outputs may not overlap
+ * inputs, each other or the workspace.
+ */
+int ssm_scan_bwd(const void* x, const void* delta, const float* delta_bias, int delta_softplus,
+                 const float* A, const void* B, const void* C, const float* D_skip,
+                 const void* z, const float* initial_state, const void* dout,
+                 const float* dlast_state, void* dx, void* ddelta, void* dz, float* dA, float* dB,
+                 float* dC, float* dD, float* ddelta_bias, float* dinitial_state, int64_t batch,
+                 int64_t seqlen, int64_t dim, int64_t dstate, int dtype, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace size ssm_scan_bwd needs (0 for invalid sizes or seqlen 0). */
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                    int dtype);
 
 /*
  * One decoding step for `batch` sequences: the recurrence above with one token.

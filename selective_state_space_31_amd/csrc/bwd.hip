@@ -1,0 +1,643 @@
+// bwd.hip -- gradients of the selective scan (the backward pass) for MI355X
+// (gfx950), behind the C ABI in include/ssm_scan.h (see there for the
+// citation and the definition of every gradient).
+//
+// The forward keeps no (b, L, D, N) states; neither does this: it recomputes
+// them, stripe by stripe (recomputation in the backward pass, as the page
+// cited in the header describes for the original kernel).  Plan, for
+// stripes of Ls <= 128 tokens:
+//   1. forward summary + carry passes (the forward's own kernels) give the
+//      state entering every stripe;
+//   2. adjoint summaries: per stripe, walked from its last token to its
+//      first from a zero adjoint, a <- (a + C_t dy_t) * e^(dt_t A), with the
+//      stripe's sum of Delta; the adjoint recurrence is linear with the same
+//      decays as the state, so
+//   3. the forward's carry kernel, fed the stripes in reverse order and
+//      started from dlast_state, gives the adjoint flowing into every
+//      stripe's last token from the tokens after it;
+//   4. main pass: per stripe, G = N/4 lanes per channel, 4 states per lane.
+//      The lane runs its stripe forward from the entering state, keeping a
+//      checkpoint of its 4 states every 16 tokens, then takes the 16-token
+//      sub-chunks from last to first: recompute the sub-chunk's states into
+//      registers, walk it backwards with the adjoint.  Per-token gradients
+//      (dx, ddelta, dz) are stored at once; dB and dC, sums over channels,
+//      are reduced across the wave's channels by lane shuffles and across
+//      the workgroup's 4 waves in LDS into one partial per workgroup;
+//      dA, dD, dbias are accumulated per stripe;
+//   5. a reduction pass adds the partials in a fixed order (no atomics: the
+//      result is bitwise reproducible run to run).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ssm_scan.h"
+
+#include "host_util.hpp"
+#include "kernels.hpp"
+
+namespace ssm {
+
+#define SSM_BWD_STATE_INSTANCES(X) \
+  X(float, 4) X(float, 8) X(float, 16) X(bf16_t, 4) X(bf16_t, 8) X(bf16_t, 16)
+#define SSM_EXTERN_STATES(TA, NT)                                                           \
+  extern template int launch_fwd_states<TA, NT, true>(const FwdArgs<TA>&, int64_t, bool, \
+                                                      hipStream_t);
+SSM_BWD_STATE_INSTANCES(SSM_EXTERN_STATES)
+
+constexpr int kBwdSub = 16;        // tokens per recomputed sub-chunk
+constexpr int kBwdMaxSub = 8;      // sub-chunks per stripe
+constexpr int kBwdThreads = 256;   // main pass workgroup: 4 waves of the same stripe
+
+template <typename TA>
+struct BwdArgs {
+  const TA* x;
+  const TA* delta;
+  const float* bias;
+  const float* A;
+  const TA* B;
+  const TA* C;
+  const float* Dsk;
+  const TA* z;
+  const float* h0;
+  const TA* dout;
+  const float* dlast;
+  TA* dx;
+  TA* ddelta;
+  TA* dz;
+  float* dh0;
+  const float* fH;  // (b, K, N, D): slot c = state entering stripe c (c >= 1)
+  float* rS;        // (b, K-1, D): slot j = sum of Delta over stripe K-1-j
+  float* rH;        // (b, K, N, D): slot K-c <- adjoint summary of stripe c; after the
+                    // carry, slot j = adjoint flowing into stripe K-1-j's last token
+  float* pB;        // (tiles, b, L, N) partial dB per workgroup tile
+  float* pC;        // (tiles, b, L, N) partial dC
+  float* pA;        // (b, K, D, N) partial dA per stripe
+  float* pD;        // (b, K, D) partial dD
+  float* pbias;     // (b, K, D) partial dbias
+  int64_t batch;
+  int L;
+  int Ls;
+  int K;
+  int dim;
+  int tiles;
+};
+
+__device__ __forceinline__ float sigmoid_f32(float u) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u * kLog2e));
+}
+
+// ----------------------------------------------------------------------------
+// 2. adjoint summaries: block (64 channels, stripe c = 1..K-1, sequence)
+// ----------------------------------------------------------------------------
+template <typename TA, int NT, bool SP, bool GATE>
+__global__ void __launch_bounds__(64) bwd_agg_kernel(BwdArgs<TA> a) {
+  const int lane = threadIdx.x;
+  const int d = blockIdx.x * 64 + lane;
+  const int c = blockIdx.y + 1;
+  const int64_t b = blockIdx.z;
+  const bool valid = d < a.dim;
+  const int dl = valid ? d : a.dim - 1;
+  float a2[NT], adj[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    a2[n] = a.A[static_cast<size_t>(dl) * NT + n] * kLog2e;
+    adj[n] = 0.0f;
+  }
+  const float bias = a.bias ? a.bias[dl] : 0.0f;
+  const int s = c * a.Ls;
+  const int e = (s + a.Ls < a.L) ? s + a.Ls : a.L;
+  float S = 0.0f;
+  for (int t = e - 1; t >= s; --t) {
+    const size_t i = (static_cast<size_t>(b) * a.L + t) * a.dim + dl;
+    const float u = to_f32(a.delta[i]) + bias;
+    const float dt = SP ? softplus_f32(u) : u;
+    S += dt;
+    const float g = to_f32(a.dout[i]);
+    const float dy = GATE ? g * silu_f32(to_f32(a.z[i])) : g;
+    float Cv[NT];
+    load_row<NT, true>(a.C + (static_cast<size_t>(b) * a.L + t) * NT, NT, Cv);
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      adj[n] = __builtin_fmaf(Cv[n], dy, adj[n]) * __builtin_amdgcn_exp2f(dt * a2[n]);
+  }
+  if (valid) {
+    a.rS[(static_cast<size_t>(b) * (a.K - 1) + (a.K - 1 - c)) * a.dim + d] = S;
+    const size_t slot = static_cast<size_t>(b) * a.K + (a.K - c);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) a.rH[(slot * NT + n) * a.dim + d] = adj[n];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// 4. main pass
+// ----------------------------------------------------------------------------
+// Four consecutive values of a (b, L, N) row: one 16-byte (float32) or
+// 8-byte (bf16) load per lane.
+__device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
+  const float4 q = *reinterpret_cast<const float4*>(p);
+  v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+}
+__device__ __forceinline__ void load4(const bf16_t* p, float (&v)[4]) {
+  const uint2 q = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(q.x << 16);
+  v[1] = __uint_as_float(q.x & 0xffff0000u);
+  v[2] = __uint_as_float(q.y << 16);
+  v[3] = __uint_as_float(q.y & 0xffff0000u);
+}
+
+// Sum over the G lanes of one channel (adjacent lanes).
+template <int G>
+__device__ __forceinline__ float sum_group(float v) {
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+// Sum over the channels of the wave (lanes with the same state group).
+template <int G>
+__device__ __forceinline__ float sum_channels(float v) {
+#pragma unroll
+  for (int o = G; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <typename TA, int NT, bool SP, bool GATE>
+__global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
+  constexpr int G = NT / 4;                  // lanes per channel
+  constexpr int CPB = kBwdThreads / G;       // channels per workgroup
+  constexpr int WAVES = kBwdThreads / 64;
+  __shared__ float red[WAVES][kBwdSub][2 * NT];
+  __shared__ float4 ckpt[kBwdMaxSub][kBwdThreads];  // per-lane checkpoints (4 states)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = tid % G;
+  const int n0 = 4 * g;
+  const int d = blockIdx.x * CPB + tid / G;
+  const int c = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const bool valid = d < a.dim;
+  const int dl = valid ? d : a.dim - 1;
+  const float vmask = valid ? 1.0f : 0.0f;
+  const int N = NT;
+  const int s = c * a.Ls;
+  const int e = (s + a.Ls < a.L) ? s + a.Ls : a.L;
+  const int len = e - s;
+
+  float Aj[4], a2[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    Aj[j] = a.A[static_cast<size_t>(dl) * N + n0 + j];
+    a2[j] = Aj[j] * kLog2e;
+  }
+  const float bias = a.bias ? a.bias[dl] : 0.0f;
+  const float dsk = a.Dsk ? a.Dsk[dl] : 0.0f;
+
+  // state entering the stripe
+  float h[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (c == 0)
+      h[j] = a.h0 ? a.h0[(static_cast<size_t>(b) * a.dim + dl) * N + n0 + j] : 0.0f;
+    else
+      h[j] = a.fH[((static_cast<size_t>(b) * a.K + c) * N + n0 + j) * a.dim + dl];
+  }
+
+  // one forward token: h <- e^(dt A) h + dt B x
+  auto fwd_step = [&](int t, float (&hh)[4]) {
+    const size_t i = (static_cast<size_t>(b) * a.L + t) * a.dim + dl;
+    const float u = to_f32(a.delta[i]) + bias;
+    const float dt = SP ? softplus_f32(u) : u;
+    const float dx = dt * to_f32(a.x[i]);
+    float Bv[4];
+    load4(a.B + (static_cast<size_t>(b) * a.L + t) * N + n0, Bv);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      hh[j] = __builtin_fmaf(__builtin_amdgcn_exp2f(dt * a2[j]), hh[j], dx * Bv[j]);
+  };
+
+  // 4a. forward over the stripe with a checkpoint every kBwdSub tokens (in
+  // LDS: each lane reads back only its own)
+  const int nsub = (len + kBwdSub - 1) / kBwdSub;
+  for (int k = 0; k < nsub; ++k) {
+    ckpt[k][tid] = make_float4(h[0], h[1], h[2], h[3]);
+    const int t1 = (s + (k + 1) * kBwdSub < e) ? s + (k + 1) * kBwdSub : e;
+    for (int t = s + k * kBwdSub; t < t1; ++t) fwd_step(t, h);
+  }
+
+  // 4b. adjoint flowing into the stripe's last token from later tokens
+  float adj[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (c == a.K - 1)
+      adj[j] = a.dlast ? a.dlast[(static_cast<size_t>(b) * a.dim + dl) * N + n0 + j] : 0.0f;
+    else
+      adj[j] = a.rH[((static_cast<size_t>(b) * a.K + (a.K - 1 - c)) * N + n0 + j) * a.dim + dl];
+  }
+  float dAacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float dDacc = 0.0f, dbacc = 0.0f;
+
+  // 4c. sub-chunks from last to first (nsub is uniform over the workgroup)
+  for (int k = nsub - 1; k >= 0; --k) {
+    const int t0 = s + k * kBwdSub;
+    float ck[4], hist[kBwdSub][4];
+    {
+      const float4 v = ckpt[k][tid];
+      ck[0] = v.x; ck[1] = v.y; ck[2] = v.z; ck[3] = v.w;
+      float hc[4] = {ck[0], ck[1], ck[2], ck[3]};
+#pragma unroll
+      for (int i = 0; i < kBwdSub; ++i) {
+        if (t0 + i < e) fwd_step(t0 + i, hc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hist[i][j] = hc[j];
+      }
+    }
+#pragma unroll
+    for (int i = kBwdSub - 1; i >= 0; --i) {
+      const int t = t0 + i;
+      float pb[4] = {0.0f, 0.0f, 0.0f, 0.0f}, pc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (t < e) {
+        const size_t ix = (static_cast<size_t>(b) * a.L + t) * a.dim + dl;
+        const size_t row = (static_cast<size_t>(b) * a.L + t) * N + n0;
+        const float u = to_f32(a.delta[ix]) + bias;
+        const float dt = SP ? softplus_f32(u) : u;
+        const float xv = to_f32(a.x[ix]);
+        float Bv[4], Cv[4];
+        load4(a.B + row, Bv);
+        load4(a.C + row, Cv);
+        float hp[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hp[j] = (i > 0) ? hist[i > 0 ? i - 1 : 0][j] : ck[j];
+        // readout of this token (all 16 states: sum over the channel's lanes)
+        float yp = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yp = __builtin_fmaf(Cv[j], hist[i][j], yp);
+        const float y = sum_group<G>(yp) + dsk * xv;
+        const float gv = to_f32(a.dout[ix]);
+        float dy = gv, dzv = 0.0f;
+        if constexpr (GATE) {
+          const float zv = to_f32(a.z[ix]);
+          const float sg = sigmoid_f32(zv);
+          dy = gv * zv * sg;
+          dzv = gv * y * sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f);
+        }
+        float s1p = 0.0f, s2p = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          adj[j] = __builtin_fmaf(Cv[j], dy, adj[j]);
+          pc[j] = dy * hist[i][j] * vmask;
+          const float dA = __builtin_amdgcn_exp2f(dt * a2[j]);
+          const float q = adj[j] * dA * hp[j];
+          dAacc[j] = __builtin_fmaf(q, dt, dAacc[j]);
+          s2p = __builtin_fmaf(Aj[j], q, s2p);
+          s1p = __builtin_fmaf(adj[j], Bv[j], s1p);
+          pb[j] = adj[j] * dt * xv * vmask;
+          adj[j] *= dA;
+        }
+        const float s1 = sum_group<G>(s1p), s2 = sum_group<G>(s2p);
+        const float ddt = __builtin_fmaf(xv, s1, s2);
+        const float dxv = __builtin_fmaf(dt, s1, dsk * dy);
+        const float dd = SP ? ddt * sigmoid_f32(u) : ddt;
+        if (g == 0 && valid) {
+          store_act(a.dx + ix, dxv);
+          store_act(a.ddelta + ix, dd);
+          if constexpr (GATE) store_act(a.dz + ix, dzv);
+        }
+        dDacc = __builtin_fmaf(dy, xv, dDacc);
+        dbacc += dd;
+      }
+      // dB, dC of this token: sum over the wave's channels
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pb[j] = sum_channels<G>(pb[j]);
+        pc[j] = sum_channels<G>(pc[j]);
+      }
+      if (lane < G) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          red[wave][i][n0 + j] = pb[j];
+          red[wave][i][NT + n0 + j] = pc[j];
+        }
+      }
+    }
+    // sum over the workgroup's waves; one partial per (tile, b, t, n)
+    __syncthreads();
+    for (int idx = tid; idx < kBwdSub * 2 * NT; idx += kBwdThreads) {
+      const int i = idx / (2 * NT);
+      const int r = idx % (2 * NT);
+      const int t = t0 + i;
+      if (t < e) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) v += red[w][i][r];
+        float* dst = r < NT ? a.pB : a.pC;
+        dst[((static_cast<size_t>(blockIdx.x) * a.batch + b) * a.L + t) * N + (r % NT)] = v;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (valid) {
+    const size_t sc = static_cast<size_t>(b) * a.K + c;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a.pA[(sc * a.dim + d) * N + n0 + j] = dAacc[j];
+    if (g == 0) {
+      a.pD[sc * a.dim + d] = dDacc;
+      a.pbias[sc * a.dim + d] = dbacc;
+    }
+    if (c == 0 && a.dh0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a.dh0[(static_cast<size_t>(b) * a.dim + d) * N + n0 + j] = adj[j];
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// 5. reductions of the partials, in a fixed order
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(const float* __restrict__ pB,
+                                                           const float* __restrict__ pC,
+                                                           float* __restrict__ dB,
+                                                           float* __restrict__ dC, int64_t per,
+                                                           int tiles) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= per) return;
+  float sb = 0.0f, scv = 0.0f;
+  for (int k = 0; k < tiles; ++k) {
+    sb += pB[k * per + i];
+    scv += pC[k * per + i];
+  }
+  dB[i] = sb;
+  dC[i] = scv;
+}
+
+// dA[d,n] = sum over (b, stripe) of pA; dD[d], dbias[d] likewise.
+__global__ void __launch_bounds__(256) bwd_reduce_params_kernel(
+    const float* __restrict__ pA, const float* __restrict__ pD, const float* __restrict__ pbias,
+    float* __restrict__ dA, float* __restrict__ dD, float* __restrict__ dbias, int dim, int N,
+    int64_t slices) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t nA = static_cast<int64_t>(dim) * N;
+  if (i < nA) {
+    float v = 0.0f;
+    for (int64_t k = 0; k < slices; ++k) v += pA[k * nA + i];
+    dA[i] = v;
+  } else if (i < nA + dim) {
+    const int64_t d = i - nA;
+    float vd = 0.0f, vb = 0.0f;
+    for (int64_t k = 0; k < slices; ++k) {
+      vd += pD[k * dim + d];
+      vb += pbias[k * dim + d];
+    }
+    if (dD) dD[d] = vd;
+    if (dbias) dbias[d] = vb;
+  }
+}
+
+// No tokens: parameter gradients are zero, dinitial_state = dlast_state.
+__global__ void __launch_bounds__(256) bwd_empty_kernel(const float* __restrict__ dlast,
+                                                       float* __restrict__ dh0, int64_t nstate,
+                                                       float* __restrict__ dA, float* dD,
+                                                       float* dbias, int dim, int N) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < nstate && dh0) dh0[i] = dlast ? dlast[i] : 0.0f;
+  if (i < static_cast<int64_t>(dim) * N) dA[i] = 0.0f;
+  if (i < dim) {
+    if (dD) dD[i] = 0.0f;
+    if (dbias) dbias[i] = 0.0f;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// host side
+// ----------------------------------------------------------------------------
+struct BwdPlan {
+  int Ls, K, tiles;
+};
+
+BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N) {
+  BwdPlan p;
+  const int G = static_cast<int>(N / 4);
+  const int cpb = kBwdThreads / G;
+  p.tiles = static_cast<int>((dim + cpb - 1) / cpb);
+  // enough workgroups for about 3 waves per SIMD, stripes of whole sub-chunks
+  const int64_t per_stripe = static_cast<int64_t>(p.tiles) * batch * (kBwdThreads / 64);
+  const int64_t target = 3LL * 4 * device_cus();
+  int64_t K = (target + per_stripe - 1) / per_stripe;
+  if (K < 1) K = 1;
+  int64_t Ls = L > 0 ? (L + K - 1) / K : kBwdSub;
+  Ls = (Ls + kBwdSub - 1) / kBwdSub * kBwdSub;
+  if (Ls > kBwdSub * kBwdMaxSub) Ls = kBwdSub * kBwdMaxSub;
+  K = L > 0 ? (L + Ls - 1) / Ls : 1;
+  p.Ls = static_cast<int>(Ls);
+  p.K = static_cast<int>(K);
+  return p;
+}
+
+struct BwdWs {
+  size_t fS, fH, rS, rH, pB, pC, pA, pD, pbias, total;
+};
+
+BwdWs bwd_layout(int64_t batch, int64_t L, int64_t dim, int64_t N, const BwdPlan& p) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  BwdWs w{};
+  const size_t K = static_cast<size_t>(p.K);
+  size_t o = 0;
+  w.fS = o; o = up(o + static_cast<size_t>(batch) * (K > 0 ? K - 1 : 0) * dim * 4);
+  w.fH = o; o = up(o + static_cast<size_t>(batch) * K * N * dim * 4);
+  w.rS = o; o = up(o + static_cast<size_t>(batch) * (K > 0 ? K - 1 : 0) * dim * 4);
+  w.rH = o; o = up(o + static_cast<size_t>(batch) * K * N * dim * 4);
+  w.pB = o; o = up(o + static_cast<size_t>(p.tiles) * batch * L * N * 4);
+  w.pC = o; o = up(o + static_cast<size_t>(p.tiles) * batch * L * N * 4);
+  w.pA = o; o = up(o + static_cast<size_t>(batch) * K * dim * N * 4);
+  w.pD = o; o = up(o + static_cast<size_t>(batch) * K * dim * 4);
+  w.pbias = o; o = up(o + static_cast<size_t>(batch) * K * dim * 4);
+  w.total = L > 0 ? o : 0;
+  return w;
+}
+
+template <typename TA, int NT>
+int launch_bwd(const BwdArgs<TA>& a, const FwdArgs<TA>& f, bool sp, bool gate, float* dA,
+               float* dB, float* dC, float* dD, float* dbias, hipStream_t s) {
+  // 1. entering states
+  int rc = launch_fwd_states<TA, NT, true>(f, a.batch, sp, s);
+  if (rc != SSM_OK) return rc;
+  // 2-3. adjoint summaries and their carry
+#define SSM_BWD_LAUNCH(KERN, GRID, BLOCK)                                                       \
+  do {                                                                                          \
+    if (sp && gate) hipLaunchKernelGGL((KERN<TA, NT, true, true>), GRID, BLOCK, 0, s, a);       \
+    else if (sp) hipLaunchKernelGGL((KERN<TA, NT, true, false>), GRID, BLOCK, 0, s, a);         \
+    else if (gate) hipLaunchKernelGGL((KERN<TA, NT, false, true>), GRID, BLOCK, 0, s, a);       \
+    else hipLaunchKernelGGL((KERN<TA, NT, false, false>), GRID, BLOCK, 0, s, a);                \
+  } while (0)
+  if (a.K > 1) {
+    const dim3 grid(static_cast<unsigned>((a.dim + 63) / 64), static_cast<unsigned>(a.K - 1),
+                    static_cast<unsigned>(a.batch));
+    SSM_BWD_LAUNCH(bwd_agg_kernel, grid, dim3(64));
+    launch_carry(f.A, a.dlast, a.rS, a.rH, nullptr, a.batch, a.dim, NT, a.K, s);
+  }
+  // 4. main pass
+  {
+    const dim3 grid(static_cast<unsigned>(a.tiles), static_cast<unsigned>(a.K),
+                    static_cast<unsigned>(a.batch));
+    SSM_BWD_LAUNCH(bwd_main_kernel, grid, dim3(kBwdThreads));
+  }
+#undef SSM_BWD_LAUNCH
+  // 5. reductions
+  const int64_t per = a.batch * a.L * NT;
+  hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(static_cast<unsigned>((per + 255) / 256)), dim3(256),
+                     0, s, a.pB, a.pC, dB, dC, per, a.tiles);
+  const int64_t np = static_cast<int64_t>(a.dim) * NT + a.dim;
+  hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3(static_cast<unsigned>((np + 255) / 256)),
+                     dim3(256), 0, s, a.pA, a.pD, a.pbias, dA, dD, dbias, a.dim, NT,
+                     a.batch * a.K);
+  return launch_status("ssm_scan_bwd");
+}
+
+template <typename TA>
+int dispatch_bwd(const BwdArgs<TA>& a, const FwdArgs<TA>& f, int N, bool sp, bool gate, float* dA,
+                 float* dB, float* dC, float* dD, float* dbias, hipStream_t s) {
+  switch (N) {
+    case 4: return launch_bwd<TA, 4>(a, f, sp, gate, dA, dB, dC, dD, dbias, s);
+    case 8: return launch_bwd<TA, 8>(a, f, sp, gate, dA, dB, dC, dD, dbias, s);
+    default: return launch_bwd<TA, 16>(a, f, sp, gate, dA, dB, dC, dD, dbias, s);
+  }
+}
+
+constexpr int64_t kBwdMaxDim = int64_t{1} << 24;
+constexpr int64_t kBwdMaxLen = (int64_t{1} << 31) - 256;
+
+}  // namespace ssm
+
+using namespace ssm;
+
+extern "C" {
+
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                    int dtype) {
+  (void)dtype;
+  if (batch < 1 || batch > 65535 || dim < 1 || dim > kBwdMaxDim || seqlen < 0 ||
+      seqlen > kBwdMaxLen || (dstate != 4 && dstate != 8 && dstate != 16))
+    return 0;
+  return bwd_layout(batch, seqlen, dim, dstate, plan_bwd(batch, seqlen, dim, dstate)).total;
+}
+
+int ssm_scan_bwd(const void* x, const void* delta, const float* delta_bias, int delta_softplus,
+                 const float* A, const void* B, const void* C, const float* D_skip, const void* z,
+                 const float* initial_state, const void* dout, const float* dlast_state, void* dx,
+                 void* ddelta, void* dz, float* dA, float* dB, float* dC, float* dD,
+                 float* ddelta_bias, float* dinitial_state, int64_t batch, int64_t seqlen,
+                 int64_t dim, int64_t dstate, int dtype, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  clear_error();
+  const char* fn = "ssm_scan_bwd";
+  if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16)
+    return fail(SSM_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+  if (delta_softplus != 0 && delta_softplus != 1)
+    return fail(SSM_ERR_UNSUPPORTED, "%s: delta_softplus must be 0 or 1, got %d", fn,
+                delta_softplus);
+  if (dstate != 4 && dstate != 8 && dstate != 16)
+    return fail(SSM_ERR_UNSUPPORTED, "%s: dstate must be 4, 8 or 16, got %lld", fn,
+                (long long)dstate);
+  if (batch < 1 || dim < 1 || seqlen < 0 || batch > 65535 || dim > kBwdMaxDim ||
+      seqlen > kBwdMaxLen)
+    return fail(SSM_ERR_SHAPE, "%s: bad sizes batch %lld, seqlen %lld, dim %lld", fn,
+                (long long)batch, (long long)seqlen, (long long)dim);
+  if (!A || !dA) return fail(SSM_ERR_NULL, "%s: A and dA are required", fn);
+  if (seqlen > 0 && (!x || !delta || !B || !C || !dout || !dx || !ddelta || !dB || !dC))
+    return fail(SSM_ERR_NULL, "%s: x, delta, B, C, dout, dx, ddelta, dB and dC are required", fn);
+  if (seqlen > 0 && z && !dz) return fail(SSM_ERR_NULL, "%s: dz is required with z", fn);
+  if (D_skip == nullptr && dD != nullptr)
+    return fail(SSM_ERR_NULL, "%s: dD given without D_skip", fn);
+  const size_t es = dtype == SSM_DTYPE_F32 ? 4 : 2;
+  const struct { const void* p; size_t k; const char* n; } al[] = {
+      {x, es, "x"}, {delta, es, "delta"}, {z, es, "z"}, {dout, es, "dout"}, {dx, es, "dx"},
+      {ddelta, es, "ddelta"}, {dz, es, "dz"}, {B, 4 * es, "B"}, {C, 4 * es, "C"}, {A, 4, "A"},
+      {D_skip, 4, "D_skip"}, {delta_bias, 4, "delta_bias"}, {initial_state, 16, "initial_state"},
+      {dlast_state, 16, "dlast_state"}, {dA, 4, "dA"}, {dB, 16, "dB"}, {dC, 16, "dC"},
+      {dD, 4, "dD"}, {ddelta_bias, 4, "ddelta_bias"}, {dinitial_state, 16, "dinitial_state"}};
+  for (const auto& e : al)
+    if (e.p && !aligned(e.p, e.k))
+      return fail(SSM_ERR_ALIGN, "%s: %s is not %zu-byte aligned", fn, e.n, e.k);
+  const size_t tok = static_cast<size_t>(batch) * seqlen * dim * es;
+  const size_t bc = static_cast<size_t>(batch) * seqlen * dstate * es;
+  const size_t bc32 = static_cast<size_t>(batch) * seqlen * dstate * 4;
+  const size_t st = static_cast<size_t>(batch) * dim * dstate * 4;
+  const size_t pd = static_cast<size_t>(dim) * 4;
+  const Span ins[] = {{x, tok, "x"}, {delta, tok, "delta"}, {z, z ? tok : 0, "z"},
+                      {dout, tok, "dout"}, {B, bc, "B"}, {C, bc, "C"},
+                      {A, static_cast<size_t>(dim) * dstate * 4, "A"},
+                      {D_skip, D_skip ? pd : 0, "D_skip"},
+                      {delta_bias, delta_bias ? pd : 0, "delta_bias"},
+                      {initial_state, initial_state ? st : 0, "initial_state"},
+                      {dlast_state, dlast_state ? st : 0, "dlast_state"}};
+  const Span outs[] = {{dx, tok, "dx"}, {ddelta, tok, "ddelta"}, {dz, dz ? tok : 0, "dz"},
+                       {dA, static_cast<size_t>(dim) * dstate * 4, "dA"}, {dB, bc32, "dB"},
+                       {dC, bc32, "dC"}, {dD, dD ? pd : 0, "dD"},
+                       {ddelta_bias, ddelta_bias ? pd : 0, "ddelta_bias"},
+                       {dinitial_state, dinitial_state ? st : 0, "dinitial_state"}};
+  for (const auto& o : outs)
+    for (const auto& i : ins)
+      if (overlap(o, i))
+        return fail(SSM_ERR_ALIAS, "%s: output %s overlaps input %s", fn, o.name, i.name);
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i)
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(SSM_ERR_ALIAS, "%s: outputs %s and %s overlap", fn, outs[i].name, outs[j].name);
+  const BwdPlan plan = plan_bwd(batch, seqlen, dim, dstate);
+  const BwdWs ws = bwd_layout(batch, seqlen, dim, dstate, plan);
+  if (workspace_bytes < ws.total || (ws.total > 0 && !workspace))
+    return fail(SSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, ws.total,
+                workspace_bytes);
+  if (ws.total > 0 && !aligned(workspace, 256))
+    return fail(SSM_ERR_ALIGN, "%s: workspace is not 256-byte aligned", fn);
+  const Span wsp{workspace, ws.total, "workspace"};
+  for (const auto& i : ins)
+    if (overlap(wsp, i)) return fail(SSM_ERR_ALIAS, "%s: workspace overlaps input %s", fn, i.name);
+  for (const auto& o : outs)
+    if (overlap(wsp, o)) return fail(SSM_ERR_ALIAS, "%s: workspace overlaps output %s", fn, o.name);
+
+  if (seqlen == 0) {
+    const int64_t n = static_cast<int64_t>(batch) * dim * dstate;
+    hipLaunchKernelGGL(bwd_empty_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                       0, stream, dlast_state, dinitial_state, n, dA, dD, ddelta_bias,
+                       static_cast<int>(dim), static_cast<int>(dstate));
+    return launch_status(fn);
+  }
+  char* w = static_cast<char*>(workspace);
+  const int K = plan.K;
+  auto wf = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+  const bool sp = delta_softplus != 0, gate = z != nullptr;
+  if (dtype == SSM_DTYPE_F32) {
+    FwdArgs<float> f{static_cast<const float*>(x), static_cast<const float*>(delta), delta_bias, A,
+                     static_cast<const float*>(B), static_cast<const float*>(C), D_skip, nullptr,
+                     nullptr, nullptr, initial_state, wf(ws.fS), wf(ws.fH), nullptr, nullptr, 0,
+                     static_cast<int>(seqlen), plan.Ls, K, static_cast<int>(dim),
+                     static_cast<int>(dstate)};
+    BwdArgs<float> a{static_cast<const float*>(x), static_cast<const float*>(delta), delta_bias,
+                     A, static_cast<const float*>(B), static_cast<const float*>(C), D_skip,
+                     static_cast<const float*>(z), initial_state, static_cast<const float*>(dout),
+                     dlast_state, static_cast<float*>(dx), static_cast<float*>(ddelta),
+                     static_cast<float*>(dz), dinitial_state, wf(ws.fH), wf(ws.rS), wf(ws.rH),
+                     wf(ws.pB), wf(ws.pC), wf(ws.pA), wf(ws.pD), wf(ws.pbias), batch,
+                     static_cast<int>(seqlen), plan.Ls, K, static_cast<int>(dim), plan.tiles};
+    return dispatch_bwd(a, f, static_cast<int>(dstate), sp, gate, dA, dB, dC, dD, ddelta_bias,
+                        stream);
+  }
+  FwdArgs<bf16_t> f{static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(delta), delta_bias, A,
+                    static_cast<const bf16_t*>(B), static_cast<const bf16_t*>(C), D_skip, nullptr,
+                    nullptr, nullptr, initial_state, wf(ws.fS), wf(ws.fH), nullptr, nullptr, 0,
+                    static_cast<int>(seqlen), plan.Ls, K, static_cast<int>(dim),
+                    static_cast<int>(dstate)};
+  BwdArgs<bf16_t> a{static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(delta), delta_bias,
+                    A, static_cast<const bf16_t*>(B), static_cast<const bf16_t*>(C), D_skip,
+                    static_cast<const bf16_t*>(z), initial_state, static_cast<const bf16_t*>(dout),
+                    dlast_state, static_cast<bf16_t*>(dx), static_cast<bf16_t*>(ddelta),
+                    static_cast<bf16_t*>(dz), dinitial_state, wf(ws.fH), wf(ws.rS), wf(ws.rH),
+                    wf(ws.pB), wf(ws.pC), wf(ws.pA), wf(ws.pD), wf(ws.pbias), batch,
+                    static_cast<int>(seqlen), plan.Ls, K, static_cast<int>(dim), plan.tiles};
+  return dispatch_bwd(a, f, static_cast<int>(dstate), sp, gate, dA, dB, dC, dD, ddelta_bias,
+                      stream);
+}
+
+}  // extern "C"

@@ -1,4 +1,4 @@
-// fwd_bf16_small.hip -- instantiates the forward launchers ((batch, seqlen) layout) for: bf16_t N=4, bf16_t N=8, bf16_t N=4 (padded), bf16_t N=16 (padded)
+// fwd_bf16_small.hip -- instantiates the forward launchers ((batch, seqlen) layout) for: bf16_t N=4, bf16_t N=8, bf16_t N=4 (padded), bf16_t N=16 (padded); also the backward's recomputation of the chunk-entering states (exact widths)
 #include "kernels.hpp"
 
 namespace ssm {
@@ -10,4 +10,6 @@ template int launch_fwd_flags<bf16_t, 4, false, false>(const FwdArgs<bf16_t>&, i
                                                   bool, hipStream_t);
 template int launch_fwd_flags<bf16_t, 16, false, false>(const FwdArgs<bf16_t>&, int64_t, bool,
                                                   bool, hipStream_t);
+template int launch_fwd_states<bf16_t, 4, true>(const FwdArgs<bf16_t>&, int64_t, bool, hipStream_t);
+template int launch_fwd_states<bf16_t, 8, true>(const FwdArgs<bf16_t>&, int64_t, bool, hipStream_t);
 }  // namespace ssm

@@ -1,4 +1,4 @@
-// fwd_f32_small.hip -- instantiates the forward launchers ((batch, seqlen) layout) for: float N=4, float N=8, float N=4 (padded), float N=16 (padded)
+// fwd_f32_small.hip -- instantiates the forward launchers ((batch, seqlen) layout) for: float N=4, float N=8, float N=4 (padded), float N=16 (padded); also the backward's recomputation of the chunk-entering states (exact widths)
 #include "kernels.hpp"
 
 namespace ssm {
@@ -10,4 +10,6 @@ template int launch_fwd_flags<float, 4, false, false>(const FwdArgs<float>&, int
                                                   bool, hipStream_t);
 template int launch_fwd_flags<float, 16, false, false>(const FwdArgs<float>&, int64_t, bool,
                                                   bool, hipStream_t);
+template int launch_fwd_states<float, 4, true>(const FwdArgs<float>&, int64_t, bool, hipStream_t);
+template int launch_fwd_states<float, 8, true>(const FwdArgs<float>&, int64_t, bool, hipStream_t);
 }  // namespace ssm

@@ -770,6 +770,21 @@ int launch_fwd(const FwdArgs<TA>& a, int64_t batch, hipStream_t s) {
   return launch_status(VL ? "ssm_scan_fwd_varlen" : "ssm_scan_fwd");
 }
 
+// The state entering every chunk (summary and carry passes only; ws_H slot
+// c holds it for c >= 1 afterwards), for the backward's recomputation.
+template <typename TA, int NT, bool EXACT>
+int launch_fwd_states(const FwdArgs<TA>& a, int64_t batch, bool sp, hipStream_t s) {
+  if (a.K <= 1) return launch_status("ssm_scan_bwd");
+  const dim3 grid(static_cast<unsigned>((a.dim + 63) / 64), static_cast<unsigned>(a.K - 1),
+                  static_cast<unsigned>(batch));
+  if (sp)
+    hipLaunchKernelGGL((fwd_agg_kernel<TA, NT, EXACT, true, false>), grid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_agg_kernel<TA, NT, EXACT, false, false>), grid, dim3(64), 0, s, a);
+  launch_carry(a.A, a.h0, a.ws_S, a.ws_H, nullptr, batch, a.dim, a.N, a.K, s);
+  return launch_status("ssm_scan_bwd");
+}
+
 template <typename TA, int NT, bool EXACT, bool VL>
 int launch_fwd_flags(const FwdArgs<TA>& a, int64_t batch, bool sp, bool gate, hipStream_t s) {
   if (sp)

@@ -22,7 +22,8 @@ STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL", -2: "SSM_ERR_SHAPE", -3: "SSM_ERR_UNS
 
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd_varlen",
            "ssm_scan_fwd_varlen_workspace_bytes", "ssm_state_update", "ssm_causal_conv1d_fwd",
-           "ssm_causal_conv1d_update", "ssm_last_error", "ssm_abi_version")
+           "ssm_causal_conv1d_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes",
+           "ssm_last_error", "ssm_abi_version")
 
 
 class SsmError(RuntimeError):
@@ -59,6 +60,11 @@ def load_library(path=LIB_PATH):
     lib.ssm_causal_conv1d_fwd.restype = I
     lib.ssm_causal_conv1d_update.argtypes = [P, P, P, P, P, I64, I64, I64, I, I, P]
     lib.ssm_causal_conv1d_update.restype = I
+    lib.ssm_scan_bwd.argtypes = [P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                 I64, I64, I64, I64, I, P, SZ, P]
+    lib.ssm_scan_bwd.restype = I
+    lib.ssm_scan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
+    lib.ssm_scan_bwd_workspace_bytes.restype = SZ
     lib.ssm_last_error.argtypes = []
     lib.ssm_last_error.restype = ctypes.c_char_p
     lib.ssm_abi_version.argtypes = []
@@ -313,3 +319,66 @@ def ssm_causal_conv1d_update(conv_state, x, weight, bias=None, silu=True, out=No
     if rc != 0:
         _raise(rc)
     return out
+
+
+def ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, dtype=torch.bfloat16):
+    return int(load_library().ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate,
+                                                           _DTYPES[dtype]))
+
+
+def ssm_scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=True,
+                 initial_state=None, dlast_state=None, grads=None, workspace=None, stream=None):
+    """Gradients of ``ssm_scan_fwd`` for the loss sum(dout*out) +
+    sum(dlast_state*last_state).  Returns a dict: dx, ddelta, dz (None
+    without z) in x's dtype; dA, dB, dC, dD (None without D), ddelta_bias,
+    dinitial_state in float32.  ``grads`` may supply preallocated outputs
+    under the same keys."""
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, seqlen, dim)")
+    batch, L, dim = x.shape
+    N = A.shape[1]
+    dev, dt = x.device, x.dtype
+    if dt not in _DTYPES:
+        raise TypeError("activations must be float32 or bfloat16, got %s" % dt)
+    f32 = torch.float32
+    _check(x, "x", (batch, L, dim), dt, dev)
+    _check(delta, "delta", (batch, L, dim), dt, dev)
+    _check(z, "z", (batch, L, dim), dt, dev, optional=True)
+    _check(dout, "dout", (batch, L, dim), dt, dev)
+    _check(B, "B", (batch, L, N), dt, dev)
+    _check(C, "C", (batch, L, N), dt, dev)
+    _check(A, "A", (dim, N), f32, dev)
+    _check(D, "D", (dim,), f32, dev, optional=True)
+    _check(delta_bias, "delta_bias", (dim,), f32, dev, optional=True)
+    _check(initial_state, "initial_state", (batch, dim, N), f32, dev, optional=True)
+    _check(dlast_state, "dlast_state", (batch, dim, N), f32, dev, optional=True)
+    g = dict(grads or {})
+    shapes = dict(dx=((batch, L, dim), dt), ddelta=((batch, L, dim), dt),
+                  dz=((batch, L, dim), dt) if z is not None else None, dA=((dim, N), f32),
+                  dB=((batch, L, N), f32), dC=((batch, L, N), f32),
+                  dD=((dim,), f32) if D is not None else None, ddelta_bias=((dim,), f32),
+                  dinitial_state=((batch, dim, N), f32))
+    for k, sd in shapes.items():
+        if sd is None:
+            g[k] = None
+            continue
+        if g.get(k) is None:
+            g[k] = torch.empty(sd[0], dtype=sd[1], device=dev)
+        _check(g[k], k, sd[0], sd[1], dev)
+    need = int(lib.ssm_scan_bwd_workspace_bytes(batch, L, dim, N, _DTYPES[dt]))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssm_scan_bwd(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                          _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(initial_state),
+                          _ptr(dout), _ptr(dlast_state), _ptr(g["dx"]), _ptr(g["ddelta"]),
+                          _ptr(g["dz"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                          _ptr(g["dD"]), _ptr(g["ddelta_bias"]), _ptr(g["dinitial_state"]),
+                          batch, L, dim, N, _DTYPES[dt], _ptr(workspace), ws_bytes,
+                          ctypes.c_void_p(stream))
+    if rc != 0:
+        _raise(rc)
+    return g

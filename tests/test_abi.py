@@ -27,7 +27,8 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd_varlen",
          "ssm_scan_fwd_varlen_workspace_bytes", "ssm_state_update", "ssm_causal_conv1d_fwd",
-         "ssm_causal_conv1d_update", "ssm_last_error", "ssm_abi_version"])
+         "ssm_causal_conv1d_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes",
+         "ssm_last_error", "ssm_abi_version"])
 
 
 def test_binding_lists_every_declared_symbol():
@@ -46,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ssm_abi_version() == 3
+    assert lib.ssm_abi_version() == 4
 
 
 def test_workspace_query_is_host_only(lib):
@@ -167,3 +168,39 @@ def test_conv_update_rejects_bad_arguments(lib):
     assert lib.ssm_causal_conv1d_update(f(4), f(1), f(2), None, f(3), 2, 64, 5, 1, 1, None) == -3
     assert lib.ssm_causal_conv1d_update(f(4), f(1), f(2), None, P(0x14000000 + 2), 2, 64, 4, 1, 1,
                                         None) == -5
+
+
+def _bwd(lib, **kw):
+    """ssm_scan_bwd with fake (never dereferenced) pointers."""
+    P = ctypes.c_void_p
+    fake = lambda k: P(0x10000000 + 0x1000000 * k)
+    a = dict(x=fake(1), delta=fake(2), bias=None, sp=1, A=fake(3), B=fake(4), C=fake(5), D=None,
+             z=None, h0=None, dout=fake(6), dlast=None, dx=fake(7), ddelta=fake(8), dz=None,
+             dA=fake(9), dB=fake(10), dC=fake(11), dD=None, dbias=None, dh0=None, batch=1, L=8,
+             dim=64, N=16, dtype=0, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.ssm_scan_bwd(a["x"], a["delta"], a["bias"], a["sp"], a["A"], a["B"], a["C"], a["D"],
+                            a["z"], a["h0"], a["dout"], a["dlast"], a["dx"], a["ddelta"], a["dz"],
+                            a["dA"], a["dB"], a["dC"], a["dD"], a["dbias"], a["dh0"], a["batch"],
+                            a["L"], a["dim"], a["N"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dA=None), -1), (dict(dout=None), -1), (dict(dB=None), -1),
+    (dict(z=ctypes.c_void_p(0x1c000000)), -1),          # z without dz
+    (dict(dD=ctypes.c_void_p(0x1d000000)), -1),         # dD without D
+    (dict(N=12), -3), (dict(N=32), -3), (dict(dtype=2), -3), (dict(batch=0), -2),
+    (dict(dB=ctypes.c_void_p(0x1a000004)), -4),
+    (dict(dx=ctypes.c_void_p(0x11000000 + 64)), -5),    # dx over x
+    (dict(dC=ctypes.c_void_p(0x1a000000 + 256)), -5),   # dC over dB
+    (dict(wsb=1), -6),                                  # workspace too small
+])
+def test_bwd_rejects_bad_arguments_before_launch(lib, kw, code):
+    assert _bwd(lib, **kw) == code
+    assert lib.ssm_last_error()
+
+
+def test_bwd_workspace_query(lib):
+    assert lib.ssm_scan_bwd_workspace_bytes(4, 2048, 1536, 16, 1) > 0
+    assert lib.ssm_scan_bwd_workspace_bytes(4, 2048, 1536, 12, 1) == 0
+    assert lib.ssm_scan_bwd_workspace_bytes(4, 0, 1536, 16, 1) == 0
