@@ -14,7 +14,8 @@ the forward kernel and the float64 oracle timed on the host as a baseline,
 plus secondary records for the other workloads (2.8B-shaped layer,
 131k-token long context, the 130M-shaped layer with a general A, the same
 tokens as packed prompts of mixed lengths, one decode step, and the causal
-convolution before the scan: forward and decode update).
+convolution before the scan: forward and decode update; the backward pass
+of the 130M-shaped layer).
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
                   [--no-secondary]
@@ -228,6 +229,48 @@ def conv_case(name, steps, warmup, torch, ops, W):
     return res
 
 
+def bwd_case(name, steps, warmup, torch, ops, W, seed=0):
+    """The backward pass (gradients of every input) on a forward workload's
+    shape: dout ~ N(0,1), no last-state gradient; outputs and workspace
+    preallocated; replicas as in fwd_case."""
+    c = dict(W.CONFIGS[name])
+    dev = torch.device("cuda:0")
+    es = 4 if c["dtype"] == "fp32" else 2
+    tc = c["batch"] * c["L"] * c["dim"]
+    tok = c["batch"] * c["L"]
+    # read x, delta, z, dout; write dx, ddelta, dz; read B, C; write dB, dC (float32)
+    alg = ((4 if c["gate"] else 3) + (3 if c["gate"] else 2)) * tc * es + \
+        2 * tok * c["dstate"] * (es + 4) + 2 * c["dim"] * c["dstate"] * 4 + 4 * c["dim"] * 4
+    R = max(1, min(4, -(-4 * MALL_BYTES // alg)))
+    probs = [W.make_problem(**c, seed=seed + r, device=dev, engine="torch_cuda") for r in range(R)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    douts = [torch.randn(p.x.shape, generator=g, device=dev).to(p.x.dtype) for p in probs]
+    grads = [None] * R
+    ws = torch.empty(ops.ssm_scan_bwd_workspace_bytes(c["batch"], c["L"], c["dim"], c["dstate"],
+                                                      probs[0].x.dtype), dtype=torch.uint8,
+                     device=dev)
+    for r in range(R):
+        grads[r] = ops.ssm_scan_bwd(probs[r].x, probs[r].delta, probs[r].A, probs[r].B, probs[r].C,
+                                    douts[r], D=probs[r].D, z=probs[r].z,
+                                    delta_bias=probs[r].delta_bias, workspace=ws)
+
+    def call(p, d, gr):
+        ops.ssm_scan_bwd(p.x, p.delta, p.A, p.B, p.C, d, D=p.D, z=p.z, delta_bias=p.delta_bias,
+                         grads=gr, workspace=ws)
+
+    total_ms, per = time_launches(call, list(zip(probs, douts, grads)), warmup, steps, torch)
+    kern_ms = sum(per) / len(per)
+    res = dict(workload=name + " backward", batch=c["batch"], seq_len=c["L"], dim=c["dim"],
+               dstate=c["dstate"], dtype=c["dtype"], input_replicas=R,
+               ms_per_step=total_ms / steps, kernel_ms_avg=kern_ms,
+               tokens_channels_per_s=tc / (kern_ms * 1e-3), algorithmic_bytes=alg,
+               achieved_GBps=alg / (kern_ms * 1e-3) / 1e9)
+    del probs, douts, grads, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def decode_case(steps, warmup, torch, ops, W):
     """One decode step of 256 sequences x 5120 channels x N=16 (float32 state,
     updated in place).  Steps rotate over several layers' states and token
@@ -343,6 +386,8 @@ def main():
             print(json.dumps(decode_case(a.steps, a.warmup, torch, ops, W)))
         elif a.only in W.VARLEN_CONFIGS:
             print(json.dumps(varlen_case(a.only, a.steps, a.warmup, torch, ops, W)))
+        elif a.only.endswith("_bwd") and a.only[:-4] in W.CONFIGS:
+            print(json.dumps(bwd_case(a.only[:-4], a.steps, a.warmup, torch, ops, W)))
         elif a.only in W.CONV_CONFIGS:
             print(json.dumps(conv_case(a.only, a.steps, a.warmup, torch, ops, W)))
         else:
@@ -374,6 +419,8 @@ def main():
         secondary["decode_fp32"] = decode_case(max(20, a.steps), 5, torch, ops, W)
         for name in W.CONV_CONFIGS:
             secondary[name] = conv_case(name, max(20, a.steps), 5, torch, ops, W)
+        secondary["mamba130m_bf16_bwd"] = bwd_case("mamba130m_bf16", max(10, a.steps // 2), 3,
+                                                   torch, ops, W)
 
     kern_ms = main_res["kernel_ms_avg"]
     achieved = main_res["algorithmic_bytes"] / (kern_ms * 1e-3) / 1e9
