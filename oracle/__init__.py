@@ -8,3 +8,5 @@ from .conv import conv1d_fwd, conv1d_update, conv_lib_path  # noqa: F401
 from .conv import build as build_conv  # noqa: F401
 from .bwd import scan_bwd, bwd_lib_path  # noqa: F401
 from .bwd import build as build_bwd  # noqa: F401
+from .ssd import ssd_scan, ssd_lib_path  # noqa: F401
+from .ssd import build as build_ssd  # noqa: F401
