@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 4
+#define SSM_SCAN_ABI_VERSION 5
 
 typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
 
@@ -187,6 +187,42 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* delta_bias, int 
 /* Workspace size ssm_scan_bwd needs (0 for invalid sizes or seqlen 0). */
 size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                                     int dtype);
+
+/*
+ * The state space dual (SSD, Mamba-2) form of the selective scan, on the
+ * matrix cores.  The pages describe it in words: with one scalar decay per
+ * head the selective SSM is a 1-semiseparable matrix (the same object as
+ * causal-masked linear attention), computed blockwise: matrix products
+ * inside chunks of 64-128 tokens, boundary states passed between chunks
+ * ("Linear Attention vs Softmax Attention: Can RWKV or Mamba Replace
+ * Transformers?" (shyankdev.com), section "Mamba (Selective State Space
+ * Models)"; "RWKV-v6 vs. Mamba-3 Selective State Spaces" (lesty.tech),
+ * sections "3.1. State Space Duality (SSD)" and "4. Hardware Acceleration";
+ * "State Space Models in Large Language Models" (llms.blog), section
+ * "Mamba-2 and Structured State Space Duality (SSD)").  Per sequence b and
+ * head h (group g = h / (nheads / ngroups) supplies B and C), with a
+ * float32 state of headdim x dstate:
+ *   dt_t = softplus(dt[b,t,h] + dt_bias[h])   (or dt + dt_bias if the flag is 0)
+ *   h_t  = e^(dt_t A[h]) h_{t-1} + dt_t x[b,t,h,:] B[b,t,g,:]^T
+ *   y[b,t,h,p] = sum_n C[b,t,g,n] h_t[p,n] + D[h] x[b,t,h,p];  out = y silu(z)
+ *   x, z, out     : (batch, seqlen, nheads, headdim) bf16; z may be NULL
+ *   dt            : (batch, seqlen, nheads) bf16, the raw step before bias/softplus
+ *   A, D, dt_bias : (nheads) float32; D and dt_bias may be NULL
+ *   B, C          : (batch, seqlen, ngroups, dstate) bf16
+ *   initial_state, last_state : (batch, nheads, headdim, dstate) float32 or NULL
+ *                   (last_state may be the initial_state buffer: resume in place)
+ *   dtype must be SSM_DTYPE_BF16, headdim 64, dstate 64 or 128, ngroups
+ *   dividing nheads; x, B, C 16-byte aligned.  No workspace.
+ * Chunks of 64 tokens; the products are bf16 matrix-core operations with
+ * float32 accumulation and a float32 state (their bf16 operands: the
+ * masked C B^T, the decay-weighted x, a bf16 copy of the state for the
+ * readout), so results match the float64 definition to bf16 accuracy.
+ */
+int ssm_ssd_fwd(const void* x, const void* dt, const float* dt_bias, int dt_softplus,
+                const float* A, const void* B, const void* C, const float* D, const void* z,
+                void* out, float* last_state, const float* initial_state, int64_t batch,
+                int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                int dtype, hipStream_t stream);
 
 /*
  * One decoding step for `batch` sequences: the recurrence above with one token.

@@ -49,6 +49,12 @@ CONV_CONFIGS = {
     "conv1d_decode_fp32": dict(batch=256, L=1, dim=5120, width=4, dtype="fp32"),
 }
 
+# The SSD (Mamba-2) form: a Mamba-2-2.7B-shaped layer (d_model 2560, expand 2:
+# 80 heads of 64 channels, dstate 128, one B/C group) over 4 x 2048 tokens.
+SSD_CONFIGS = {
+    "ssd_mamba2_2p7b_bf16": dict(batch=4, L=2048, H=80, P=64, N=128, G=1, gate=True),
+}
+
 # Packed variable-length prefill: the 130M-shaped layer's 8192 tokens as a
 # batch of prompts of mixed lengths (log-uniform in [64, 4096], drawn from
 # ``seed``) concatenated without padding; fresh prompts (zero initial state),
@@ -331,3 +337,44 @@ def make_conv_problem(batch, L, dim, width=4, dtype="fp32", seed=0, device="cpu"
         raise ValueError(engine)
     return Problem(batch=batch, L=L, dim=dim, width=width, dtype=dtype, x=x, weight=w,
                    bias=bias if with_bias else None, state0=st)
+
+
+def make_ssd_problem(batch, L, H, P, N, G=1, gate=True, dt_range=(1e-3, 1e-1), seed=0,
+                     device="cpu", engine="numpy", initial_state=False, with_D=True,
+                     with_bias=True, dt_softplus=True, **_):
+    """Inputs of the SSD form: per head a step size log-uniform in dt_range
+    (bias = inverse softplus), dt = 0.5 N(0,1), A[h] = -U(1, 16) (Mamba-2's
+    range of decay rates), D = 1; x, z, B, C ~ N(0,1) in bf16; state ~
+    N(0,1).  Draw order: step sizes, A, x, z, B, C, dt, state."""
+    lo, hi = dt_range
+    bf = torch.bfloat16
+    if engine == "numpy":
+        rng = np.random.default_rng(seed + 6700417)
+        dts = np.exp(rng.uniform(math.log(lo), math.log(hi), size=H))
+        A = -rng.uniform(1.0, 16.0, size=H).astype(np.float32)
+        f = lambda *s: torch.from_numpy(rng.standard_normal(s, dtype=np.float32))
+        x, z, B, C = f(batch, L, H, P), f(batch, L, H, P), f(batch, L, G, N), f(batch, L, G, N)
+        dt = 0.5 * f(batch, L, H)
+        h0 = f(batch, H, P, N) if initial_state else None
+        mv = lambda t, dtp=bf: None if t is None else t.to(dtp).to(device)
+        x, z, B, C, dt = (mv(t) for t in (x, z, B, C, dt))
+        h0 = mv(h0, torch.float32)
+        A = torch.from_numpy(A).to(device)
+    elif engine == "torch_cuda":
+        g = torch.Generator(device=device)
+        g.manual_seed(seed + 6700417)
+        dts = torch.exp(torch.empty(H, dtype=torch.float64, device=device).uniform_(
+            math.log(lo), math.log(hi), generator=g)).cpu().numpy()
+        A = -torch.empty(H, device=device).uniform_(1.0, 16.0, generator=g)
+        rn = lambda *s: torch.randn(*s, generator=g, device=device)
+        x, z, B, C = rn(batch, L, H, P).to(bf), rn(batch, L, H, P).to(bf), rn(batch, L, G, N).to(bf), \
+            rn(batch, L, G, N).to(bf)
+        dt = (0.5 * rn(batch, L, H)).to(bf)
+        h0 = rn(batch, H, P, N) if initial_state else None
+    else:
+        raise ValueError(engine)
+    bias = torch.from_numpy(_bias_from_dt(dts).astype(np.float32)).to(device)
+    return Problem(batch=batch, L=L, H=H, P=P, N=N, G=G, dt_softplus=dt_softplus, x=x,
+                   z=z if gate else None, B=B, C=C, dt=dt, A=A,
+                   D=torch.ones(H, dtype=torch.float32, device=device) if with_D else None,
+                   dt_bias=bias if with_bias else None, h0=h0)

@@ -28,7 +28,7 @@ def test_header_declares_the_expected_entry_points():
         ["ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd_varlen",
          "ssm_scan_fwd_varlen_workspace_bytes", "ssm_state_update", "ssm_causal_conv1d_fwd",
          "ssm_causal_conv1d_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes",
-         "ssm_last_error", "ssm_abi_version"])
+         "ssm_ssd_fwd", "ssm_last_error", "ssm_abi_version"])
 
 
 def test_binding_lists_every_declared_symbol():
@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ssm_abi_version() == 4
+    assert lib.ssm_abi_version() == 5
 
 
 def test_workspace_query_is_host_only(lib):

@@ -1,0 +1,114 @@
+"""GPU parity of the SSD (Mamba-2) form (ssm_ssd_fwd) with its float64
+oracle.
+
+The kernel computes the duality's matrix side on the matrix cores (bf16
+operands, float32 accumulation and state); the oracle is the recurrence.
+Outputs are bf16; the comparison is |gpu - ref| <= rtol |ref| + atol
+max|ref| with the bf16 tolerances (rtol 2e-2, atol 1e-2 relative to the
+largest magnitude: the bf16 operands of the products are rounded to 2^-9
+relative, and the sums over up to 128 states and 64 tokens scale with the
+output's range).  Cases cover one and many chunks, ragged last chunks,
+both state widths, several groups, every optional input, resume in place,
+and the Mamba-2-2.7B-shaped layer on sampled heads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from selective_state_space_31_amd import ssm_ssd_fwd
+from selective_state_space_31_amd.workloads import SSD_CONFIGS, make_ssd_problem
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def host(t):
+    return None if t is None else t.to(torch.float32).cpu().numpy()
+
+
+def close(got, ref, what, rtol=2e-2, atol=1e-2):
+    got = np.asarray(got, np.float64)
+    at = atol * max(1.0, float(np.max(np.abs(ref)))) if ref.size else atol
+    err = np.abs(got - ref)
+    bad = err > at + rtol * np.abs(ref)
+    assert np.isfinite(got).all(), what + ": non-finite"
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - at - rtol * np.abs(ref)), err.shape)
+        raise AssertionError("%s: %d of %d outside; worst at %s got %r ref %r (atol %g)"
+                             % (what, int(bad.sum()), bad.size, i, got[i], ref[i], at))
+
+
+def run_and_compare(p, what, heads=None):
+    print("case:", what, flush=True)
+    out, last = ssm_ssd_fwd(p.x, p.dt, p.A, p.B, p.C, D=p.D, z=p.z, dt_bias=p.dt_bias,
+                            dt_softplus=p.dt_softplus, initial_state=p.h0, return_last_state=True)
+    torch.cuda.synchronize()
+    hs = slice(None) if heads is None else heads
+    sub = lambda t, ax: None if t is None else (t if heads is None else t.index_select(ax, heads))
+    G = p.G
+    if heads is not None:
+        assert G == 1
+    ref, ref_last = oracle.ssd_scan(host(sub(p.x, 2)), host(sub(p.dt, 2)), host(sub(p.A, 0)),
+                                    host(p.B), host(p.C), D=host(sub(p.D, 0)), z=host(sub(p.z, 2)),
+                                    dt_bias=host(sub(p.dt_bias, 0)), dt_softplus=p.dt_softplus,
+                                    h0=host(sub(p.h0, 1)))
+    got = out if heads is None else out.index_select(2, heads)
+    gl = last if heads is None else last.index_select(1, heads)
+    close(host(got), ref, what + " out")
+    close(host(gl), ref_last, what + " last_state")
+    return out, last
+
+
+SHAPES = [  # (batch, L, H, N, G)
+    (1, 1, 1, 64, 1), (2, 63, 2, 64, 1), (1, 64, 3, 128, 1), (2, 65, 2, 128, 1),
+    (1, 300, 4, 64, 2), (2, 257, 6, 128, 3), (1, 1000, 2, 128, 1),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b%d_L%d_H%d_N%d_G%d" % s)
+def test_shapes(shape):
+    b, L, H, N, G = shape
+    p = make_ssd_problem(b, L, H, 64, N, G, seed=L + H + N, device=DEV, initial_state=True)
+    run_and_compare(p, "shape %s" % (shape,))
+
+
+FLAGS = [dict(gate=False), dict(with_D=False), dict(with_bias=False), dict(initial_state=False),
+         dict(dt_softplus=False), dict(gate=False, with_D=False, with_bias=False,
+                                       initial_state=False)]
+
+
+@pytest.mark.parametrize("flags", FLAGS, ids=lambda f: "-".join("%s=%s" % kv for kv in f.items()))
+def test_optional_inputs(flags):
+    kw = dict(gate=True, initial_state=True)
+    kw.update(flags)
+    p = make_ssd_problem(2, 200, 3, 64, 128, 1, seed=17, device=DEV, **kw)
+    if not p.dt_softplus:
+        p.dt = (p.dt.float().abs() * 0.05 + 0.001).to(torch.bfloat16)
+        p.dt_bias = torch.full_like(p.dt_bias, 0.01) if p.dt_bias is not None else None
+    run_and_compare(p, "flags %s" % flags)
+
+
+def test_resume_in_place_and_split():
+    p = make_ssd_problem(1, 200, 2, 64, 128, 1, seed=19, device=DEV, initial_state=True)
+    full, last = ssm_ssd_fwd(p.x, p.dt, p.A, p.B, p.C, D=p.D, z=p.z, dt_bias=p.dt_bias,
+                             initial_state=p.h0, return_last_state=True)
+    st = p.h0.clone()
+    parts = []
+    for a, b in ((0, 70), (70, 200)):
+        sl = lambda t: t[:, a:b].contiguous()
+        o, _ = ssm_ssd_fwd(sl(p.x), sl(p.dt), p.A, sl(p.B), sl(p.C), D=p.D, z=sl(p.z),
+                           dt_bias=p.dt_bias, initial_state=st, last_state=st)
+        parts.append(o)
+    torch.cuda.synchronize()
+    ref, ref_last = oracle.ssd_scan(host(p.x), host(p.dt), host(p.A), host(p.B), host(p.C),
+                                    D=host(p.D), z=host(p.z), dt_bias=host(p.dt_bias), h0=host(p.h0))
+    close(host(torch.cat(parts, 1)), ref, "split out")
+    close(host(st), ref_last, "split last_state")
+
+
+def test_config_ssd_mamba2_2p7b_bf16_sampled_heads():
+    c = SSD_CONFIGS["ssd_mamba2_2p7b_bf16"]
+    p = make_ssd_problem(**c, seed=0, device=DEV, engine="torch_cuda")
+    heads = torch.tensor([0, 1, 37, 79], device=DEV)
+    run_and_compare(p, "ssd_mamba2_2p7b_bf16 (4 heads)", heads=heads)
