@@ -15,7 +15,8 @@ plus secondary records for the other workloads (2.8B-shaped layer,
 131k-token long context, the 130M-shaped layer with a general A, the same
 tokens as packed prompts of mixed lengths, one decode step, and the causal
 convolution before the scan: forward and decode update; the backward pass
-of the 130M-shaped layer).
+of the 130M-shaped layer; the SSD (Mamba-2) form of a 2.7B-shaped layer on
+the matrix cores).
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
                   [--no-secondary]
@@ -271,6 +272,49 @@ def bwd_case(name, steps, warmup, torch, ops, W, seed=0):
     return res
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+
+
+def ssd_case(name, steps, warmup, torch, ops, W, seed=0):
+    """The SSD (Mamba-2) form on the matrix cores: one ssm_ssd_fwd call over
+    the configured layer (replicas as in fwd_case).  Flops are those of the
+    four chunk products per (sequence, chunk of 64, head); bytes every
+    input and output once."""
+    c = dict(W.SSD_CONFIGS[name])
+    dev = torch.device("cuda:0")
+    Q = 64
+    tok = c["batch"] * c["L"]
+    nchunks = -(-c["L"] // Q)
+    flops = 2 * c["batch"] * nchunks * c["H"] * (Q * Q * c["N"] + Q * Q * c["P"] +
+                                                 2 * Q * c["N"] * c["P"])
+    alg = (tok * c["H"] * c["P"] * 2 * (3 if c["gate"] else 2) + tok * c["H"] * 2 +
+           2 * tok * c["G"] * c["N"] * 2 + 3 * c["H"] * 4)
+    R = max(1, min(8, -(-4 * MALL_BYTES // alg)))
+    probs = [W.make_ssd_problem(**c, seed=seed + r, device=dev, engine="torch_cuda")
+             for r in range(R)]
+    outs = [torch.empty_like(p.x) for p in probs]
+
+    def call(p, o):
+        ops.ssm_ssd_fwd(p.x, p.dt, p.A, p.B, p.C, D=p.D, z=p.z, dt_bias=p.dt_bias, out=o)
+
+    total_ms, per = time_launches(call, list(zip(probs, outs)), warmup, steps, torch)
+    kern_ms = sum(per) / len(per)
+    tf = flops / (kern_ms * 1e-3) / 1e12
+    gbps = alg / (kern_ms * 1e-3) / 1e9
+    res = dict(workload=name, batch=c["batch"], seq_len=c["L"], nheads=c["H"], headdim=c["P"],
+               dstate=c["N"], ngroups=c["G"], gate=c["gate"], dtype="bf16", input_replicas=R,
+               ms_per_step=total_ms / steps, kernel_ms_avg=kern_ms,
+               tokens_channels_per_s=tok * c["H"] * c["P"] / (kern_ms * 1e-3),
+               algorithmic_flops=flops, algorithmic_bytes=alg,
+               roofline_mfma=dict(bound="mfma", achieved=round(tf, 1), peak=MFMA_BF16_PEAK_TFLOPS,
+                                  unit="TFLOP/s", frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4)),
+               roofline_hbm=dict(bound="hbm", achieved=round(gbps, 1), peak=HBM_PEAK_GBPS,
+                                 unit="GB/s", frac=round(gbps / HBM_PEAK_GBPS, 4)))
+    del probs, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 def decode_case(steps, warmup, torch, ops, W):
     """One decode step of 256 sequences x 5120 channels x N=16 (float32 state,
     updated in place).  Steps rotate over several layers' states and token
@@ -388,6 +432,8 @@ def main():
             print(json.dumps(varlen_case(a.only, a.steps, a.warmup, torch, ops, W)))
         elif a.only.endswith("_bwd") and a.only[:-4] in W.CONFIGS:
             print(json.dumps(bwd_case(a.only[:-4], a.steps, a.warmup, torch, ops, W)))
+        elif a.only in W.SSD_CONFIGS:
+            print(json.dumps(ssd_case(a.only, a.steps, a.warmup, torch, ops, W)))
         elif a.only in W.CONV_CONFIGS:
             print(json.dumps(conv_case(a.only, a.steps, a.warmup, torch, ops, W)))
         else:
@@ -421,6 +467,8 @@ def main():
             secondary[name] = conv_case(name, max(20, a.steps), 5, torch, ops, W)
         secondary["mamba130m_bf16_bwd"] = bwd_case("mamba130m_bf16", max(10, a.steps // 2), 3,
                                                    torch, ops, W)
+        for name in W.SSD_CONFIGS:
+            secondary[name] = ssd_case(name, max(10, a.steps // 2), 3, torch, ops, W)
 
     kern_ms = main_res["kernel_ms_avg"]
     achieved = main_res["algorithmic_bytes"] / (kern_ms * 1e-3) / 1e9

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 5
+#define SSM_SCAN_ABI_VERSION 6
 
 typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
 
@@ -212,7 +212,10 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  *   initial_state, last_state : (batch, nheads, headdim, dstate) float32 or NULL
  *                   (last_state may be the initial_state buffer: resume in place)
  *   dtype must be SSM_DTYPE_BF16, headdim 64, dstate 64 or 128, ngroups
- *   dividing nheads; x, B, C 16-byte aligned.  No workspace.
+ *   dividing nheads; x, B, C 16-byte aligned.
+ *   workspace: at least ssm_ssd_fwd_workspace_bytes(...) bytes, 256-byte
+ *   aligned (may be NULL when that size is 0: when (batch, head) pairs
+ *   already fill the device the sequence is not cut into segments).
  * Chunks of 64 tokens; the products are bf16 matrix-core operations with
  * float32 accumulation and a float32 state (their bf16 operands: the
  * masked C B^T, the decay-weighted x, a bf16 copy of the state for the
@@ -222,7 +225,11 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* dt_bias, int dt_soft
                 const float* A, const void* B, const void* C, const float* D, const void* z,
                 void* out, float* last_state, const float* initial_state, int64_t batch,
                 int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
-                int dtype, hipStream_t stream);
+                int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace size ssm_ssd_fwd needs (0 when none, or for invalid sizes). */
+size_t ssm_ssd_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads,
+                                   int64_t headdim, int64_t dstate, int64_t ngroups);
 
 /*
  * One decoding step for `batch` sequences: the recurrence above with one token.

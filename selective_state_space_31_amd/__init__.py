@@ -8,7 +8,7 @@ include/ssm_scan.h; the work runs in hand-written gfx950 HIP kernels
 """
 _OPS = ("ssm_scan_fwd", "ssm_scan_fwd_varlen", "ssm_state_update", "ssm_scan_fwd_workspace_bytes",
         "ssm_scan_fwd_varlen_workspace_bytes", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
-        "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_ssd_fwd",
+        "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_ssd_fwd", "ssm_ssd_fwd_workspace_bytes",
         "ssm_last_error", "ssm_abi_version",
         "load_library", "SsmError", "LIB_PATH", "EXPORTS")
 

@@ -23,7 +23,7 @@ STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL", -2: "SSM_ERR_SHAPE", -3: "SSM_ERR_UNS
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd_varlen",
            "ssm_scan_fwd_varlen_workspace_bytes", "ssm_state_update", "ssm_causal_conv1d_fwd",
            "ssm_causal_conv1d_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes",
-           "ssm_ssd_fwd", "ssm_last_error", "ssm_abi_version")
+           "ssm_ssd_fwd", "ssm_ssd_fwd_workspace_bytes", "ssm_last_error", "ssm_abi_version")
 
 
 class SsmError(RuntimeError):
@@ -66,8 +66,10 @@ def load_library(path=LIB_PATH):
     lib.ssm_scan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.ssm_scan_bwd_workspace_bytes.restype = SZ
     lib.ssm_ssd_fwd.argtypes = [P, P, P, I, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I,
-                                P]
+                                P, SZ, P]
     lib.ssm_ssd_fwd.restype = I
+    lib.ssm_ssd_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64]
+    lib.ssm_ssd_fwd_workspace_bytes.restype = SZ
     lib.ssm_last_error.argtypes = []
     lib.ssm_last_error.restype = ctypes.c_char_p
     lib.ssm_abi_version.argtypes = []
@@ -387,9 +389,14 @@ def ssm_scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta
     return g
 
 
+def ssm_ssd_fwd_workspace_bytes(batch, seqlen, nheads, headdim, dstate, ngroups=1):
+    return int(load_library().ssm_ssd_fwd_workspace_bytes(batch, seqlen, nheads, headdim, dstate,
+                                                          ngroups))
+
+
 def ssm_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True,
                 initial_state=None, return_last_state=False, out=None, last_state=None,
-                stream=None):
+                workspace=None, stream=None):
     """SSD (Mamba-2) forward: x, z (batch, seqlen, nheads, headdim) bf16;
     dt (batch, seqlen, nheads) bf16; A, D, dt_bias (nheads,) float32; B, C
     (batch, seqlen, ngroups, dstate) bf16; states (batch, nheads, headdim,
@@ -418,12 +425,16 @@ def ssm_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True,
     if last_state is None and return_last_state:
         last_state = torch.empty((batch, H, P, N), dtype=f32, device=dev)
     _check(last_state, "last_state", (batch, H, P, N), f32, dev, optional=True)
+    need = int(lib.ssm_ssd_fwd_workspace_bytes(batch, L, H, P, N, G))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     rc = lib.ssm_ssd_fwd(_ptr(x), _ptr(dt), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(A), _ptr(B),
                          _ptr(C), _ptr(D), _ptr(z), _ptr(out), _ptr(last_state),
-                         _ptr(initial_state), batch, L, H, P, N, G, _DTYPES[dt_],
-                         ctypes.c_void_p(stream))
+                         _ptr(initial_state), batch, L, H, P, N, G, _DTYPES[dt_], _ptr(workspace),
+                         ws_bytes, ctypes.c_void_p(stream))
     if rc != 0:
         _raise(rc)
     if last_state is not None:

@@ -28,7 +28,7 @@ def test_header_declares_the_expected_entry_points():
         ["ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd_varlen",
          "ssm_scan_fwd_varlen_workspace_bytes", "ssm_state_update", "ssm_causal_conv1d_fwd",
          "ssm_causal_conv1d_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes",
-         "ssm_ssd_fwd", "ssm_last_error", "ssm_abi_version"])
+         "ssm_ssd_fwd", "ssm_ssd_fwd_workspace_bytes", "ssm_last_error", "ssm_abi_version"])
 
 
 def test_binding_lists_every_declared_symbol():
@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ssm_abi_version() == 5
+    assert lib.ssm_abi_version() == 6
 
 
 def test_workspace_query_is_host_only(lib):
@@ -204,3 +204,27 @@ def test_bwd_workspace_query(lib):
     assert lib.ssm_scan_bwd_workspace_bytes(4, 2048, 1536, 16, 1) > 0
     assert lib.ssm_scan_bwd_workspace_bytes(4, 2048, 1536, 12, 1) == 0
     assert lib.ssm_scan_bwd_workspace_bytes(4, 0, 1536, 16, 1) == 0
+
+
+def _ssd(lib, **kw):
+    """ssm_ssd_fwd with fake (never dereferenced) pointers."""
+    P = ctypes.c_void_p
+    fake = lambda k: P(0x10000000 + 0x1000000 * k)
+    a = dict(x=fake(1), dt=fake(2), bias=None, sp=1, A=fake(3), B=fake(4), C=fake(5), D=None,
+             z=None, out=fake(6), last=None, h0=None, batch=1, L=64, H=2, P=64, N=128, G=1,
+             dtype=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.ssm_ssd_fwd(a["x"], a["dt"], a["bias"], a["sp"], a["A"], a["B"], a["C"], a["D"],
+                           a["z"], a["out"], a["last"], a["h0"], a["batch"], a["L"], a["H"], a["P"],
+                           a["N"], a["G"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), -3), (dict(P=32), -3), (dict(N=96), -3), (dict(G=3), -2), (dict(H=0), -2),
+    (dict(A=None), -1), (dict(x=None), -1), (dict(x=ctypes.c_void_p(0x11000008)), -4),
+    (dict(out=ctypes.c_void_p(0x11000000 + 64)), -5),
+    (dict(L=8192), -6),                              # segmented: needs a workspace
+])
+def test_ssd_rejects_bad_arguments_before_launch(lib, kw, code):
+    assert _ssd(lib, **kw) == code
+    assert lib.ssm_last_error()
