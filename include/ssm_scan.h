@@ -212,7 +212,7 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  *   initial_state, last_state : (batch, nheads, headdim, dstate) float32 or NULL
  *                   (last_state may be the initial_state buffer: resume in place)
  *   dtype must be SSM_DTYPE_BF16, headdim 64, dstate 64 or 128, ngroups
- *   dividing nheads; x, B, C 16-byte aligned.
+ *   dividing nheads; x, B, C 16-byte aligned, z and out 8-byte aligned.
  *   workspace: at least ssm_ssd_fwd_workspace_bytes(...) bytes, 256-byte
  *   aligned (may be NULL when that size is 0: when (batch, head) pairs
  *   already fill the device the sequence is not cut into segments).

@@ -3,26 +3,48 @@
 // there for the citation and the definition).
 //
 // With one scalar decay per head the sequence map is 1-semiseparable, so a
-// chunk of Q tokens is computed by matrix products (per sequence b, head h,
-// with lambda_t = sum of dt A over the chunk up to t):
+// chunk of Q = 64 tokens is computed by matrix products (per sequence b,
+// head h, with lambda_t = sum of dt A over the chunk up to t):
 //   S      = (C B^T) o mask,  mask[t,s] = e^(lambda_t - lambda_s) dt_s for s <= t
 //   Y      = S X + diag(e^lambda) (C h^T) + D X,  then the gate
 //   h     <- e^(lambda_end) h + X_w^T B,  X_w[s,:] = X[s,:] dt_s e^(lambda_end - lambda_s)
-// where h (headdim x dstate) is the state entering the chunk.  The four
-// products are bf16 MFMA (v_mfma_f32_32x32x16_bf16) with float32
-// accumulation.  One workgroup (4 waves) owns one (b, h, segment of
-// chunks) and walks its chunks in order; the float32 state lives in the
-// MFMA accumulators of the four waves (no per-chunk states in memory).  Per
-// chunk the operands are staged in LDS: C and B row-major, x transposed,
-// the masked S, and a bf16 copy of the state.  When (b, h) pairs alone do
-// not fill the chip, the sequence is cut into segments: a state pass runs
-// each segment but the last from zero (state update only), a carry pass
-// chains the segments' end states, and the output pass starts every
-// segment from its entering state.
+// where h (headdim x dstate) is the state entering the chunk.  The products
+// are bf16 MFMA (v_mfma_f32_16x16x32_bf16) with float32 accumulation.
 //
-// MFMA operand layout (32x32x16 bf16; checked on the device): lane l holds
-// A[l%32][8*(l/32) + i] and B[8*(l/32) + i][l%32], i = 0..7; accumulator
-// element r of lane l is D[8*(r/4) + 4*(l/32) + r%4][l%32].
+// Work split.  One workgroup (4 waves) owns one (b, h, segment of chunks)
+// and walks its chunks in order.  Wave w owns the 16 head channels
+// p in [16w, 16w+16): it keeps the float32 state h[p][:] for those channels
+// in its MFMA accumulators (as h^T tiles of 16 state rows x 16 channels),
+// computes Y^T for them (Y^T = X^T S^T + H C^T ...) and updates their state.
+// Because the readout term H C^T takes H as the A operand straight from the
+// wave's own accumulators, the state never goes through LDS.  The masked S
+// is the one product the waves share: its ten non-zero 16x16 tiles (s <= t)
+// are split over the waves and staged in LDS as bf16.
+//
+// LDS holds the chunk's B, C and x row-major (token rows) as they arrive
+// from HBM, with the 16-byte pieces of each row XOR-swizzled by the row
+// index so that the MFMA operand reads hit distinct banks.  The operands
+// that need a token-contiguous layout (B^T and X^T, whose contraction index
+// is the token) are read with the gfx950 transpose load ds_read_b64_tr_b16.
+// All global traffic goes through buffer descriptors based at the chunk's
+// first row: per-lane offsets are loop constants, the row stride steps are
+// scalar offsets, and rows past the sequence end fall outside the
+// descriptor's range (loads read zero, stores are dropped).  The next
+// chunk's inputs are fetched into registers while the current one is
+// computed.
+//
+// When (b, h) pairs alone do not fill the chip, the sequence is cut into
+// segments: a state pass runs every segment but the last from a zero state
+// (state update only) and leaves its end state and total log-decay; the
+// output pass of segment s starts from the state entering it, composed from
+// the initial state and the end states of segments 0..s-1.
+//
+// MFMA operand layout (16x16x32 bf16; checked on the device): lane l holds
+// A[l%16][8*(l/16) + i] and B[8*(l/16) + i][l%16], i = 0..7; accumulator
+// element r of lane l is D[4*(l/16) + r][l%16].  ds_read_b64_tr_b16 (checked
+// on the device, arbitrary per-lane addresses): within each 16-lane group,
+// lane 4b+j receives element j of the 8 bytes addressed by lane 4k+b, as its
+// element k (k, b, j = 0..3).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -35,12 +57,21 @@
 namespace ssm {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kSsdQ = 64;        // chunk length (tokens)
-constexpr int kSsdP = 64;        // head dimension
+constexpr int kSsdQ = 64;         // chunk length (tokens)
+constexpr int kSsdP = 64;         // head dimension
 constexpr int kSsdThreads = 256;  // 4 waves
-constexpr int kSsdPad = 8;       // LDS row padding (bf16 elements)
+
+#ifndef SSM_SSD_WG_PER_CU
+#define SSM_SSD_WG_PER_CU 3  // workgroups per compute unit the segment plan aims for
+#endif
 
 struct SsdArgs {
   const bf16_t* x;
@@ -54,66 +85,168 @@ struct SsdArgs {
   bf16_t* out;
   float* last_state;
   const float* h0;
-  float* seg_state;  // (batch, nseg, H, P, N): end state of segment s (state pass), then
-                     // (after the carry) the state entering segment s
-  float* seg_lam;    // (batch, nseg, H): sum of dt A over segment s
+  float* seg_state;  // (batch, nseg-1, H) blocks of P*N floats: end state of segment s
+                     // run from zero, in the waves' accumulator order
+  float* seg_lam;    // (batch, nseg-1, H): sum of dt A over segment s
   int L;
   int H;
   int G;
   int softplus;
-  int cps;   // chunks per segment
+  int cps;  // chunks per segment
   int nseg;
 };
 
-__device__ __forceinline__ __bf16 to_bf(float v) { return static_cast<__bf16>(v); }
-__device__ __forceinline__ float from_bf(__bf16 v) { return static_cast<float>(v); }
 __device__ __forceinline__ float exp_f(float v) { return __builtin_amdgcn_exp2f(v * kLog2e); }
 
-// Row/column of accumulator element r of this lane within a 32x32 tile.
-__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r / 4) + 4 * (lane / 32) + (r % 4); }
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x8 lds_b128(const unsigned char* base, int byte) {
+  return *reinterpret_cast<const bf16x8*>(base + byte);
+}
+
+// transpose load (see the header comment for its lane mapping)
+__device__ __forceinline__ s16x4 lds_tr(unsigned char* base, int byte) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + byte));
+}
+
+__device__ __forceinline__ bf16x8 cat8(s16x4 lo, s16x4 hi) {
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// XOR swizzles of the 16-byte piece index of an LDS row (they change only
+// the low three bits, i.e. the bank group within 128 bytes).
+//  B, C rows: bits 1 and 2 of (row % 8) swapped.  Eight consecutive rows
+//    get distinct pieces (row reads of the products are conflict free), and
+//    rows 4i..4i+3 get {0,1,4,5} or {2,3,6,7}: with the alternating 8-byte
+//    halves of the state tiles (below) the transpose loads of B^T are too.
+__device__ __forceinline__ int swz_bc(int r) { return (r & 1) | ((r & 2) << 1) | ((r & 4) >> 1); }
+//  x rows (128 bytes): 2 (row % 4) + bit 2 of the row, for the transpose loads of X^T.
+__device__ __forceinline__ int swz_x(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+//  S rows (128 bytes): row % 8.
+__device__ __forceinline__ int swz_s(int r) { return r & 7; }
+
+// State tile nb of a wave holds h^T rows n = nmap(nb, q) + r for the lanes
+// of group q (accumulator elements r = 0..3): the two tiles 2i, 2i+1 of a
+// group cover the eight consecutive n = 32i + 8q .. +7, the lower four in
+// tile 2i for even q and in tile 2i+1 for odd q.
+__device__ __forceinline__ int nmap(int nb, int q) {
+  return 32 * (nb >> 1) + 8 * q + 4 * ((nb & 1) ^ (q & 1));
+}
+
+// Tiles (sb, tb0..tb0+NTB-1) of S^T (rows s in 16 sb, columns t in 16 tb):
+// S^T = B C^T masked and scaled, written to sS as S[t][s] in bf16.
+template <int NS, int NTB>
+__device__ __forceinline__ void ssd_s_tiles(const unsigned char* sB, const unsigned char* sC,
+                                            unsigned char* sS, const float* slam,
+                                            const float* sdt, const int (&bc_base)[2], int lane,
+                                            int sb, int tb0) {
+  constexpr int RB = NS * 2;
+  const int m = lane & 15, q = lane >> 4;
+  f32x4 acc[NTB];
+#pragma unroll
+  for (int i = 0; i < NTB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < NS / 32; ++kk) {
+    const int off = bc_base[kk & 1] + 128 * (kk >> 1);
+    const bf16x8 av = lds_b128(sB, off + 16 * RB * sb);
+#pragma unroll
+    for (int i = 0; i < NTB; ++i) {
+      const bf16x8 bv = lds_b128(sC, off + 16 * RB * (tb0 + i));
+      acc[i] = mfma16(av, bv, acc[i]);
+    }
+  }
+  const int s0 = 16 * sb + 4 * q;
+  const f32x4 ls = *reinterpret_cast<const f32x4*>(&slam[s0]);
+  const f32x4 ds = *reinterpret_cast<const f32x4*>(&sdt[s0]);
+#pragma unroll
+  for (int i = 0; i < NTB; ++i) {
+    const int tb = tb0 + i, t = 16 * tb + m;
+    const float lt = slam[t];
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float e = acc[i][r] * exp_f(lt - ls[r]) * ds[r];
+      v[r] = (tb > sb || 4 * q + r <= m) ? e : 0.0f;
+    }
+    const u32x2 pk = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+    *reinterpret_cast<u32x2*>(sS + t * 128 + (((2 * sb + (q >> 1)) ^ swz_s(t)) << 4) +
+                              8 * (q & 1)) = pk;
+  }
+}
 
 // FULL: outputs (and the last segment's final state); otherwise the state
 // pass: only the state update, from zero, leaving the segment's end state
-// and total log-decay for the carry.  Block (head, segment, sequence).
+// and total log-decay.  Block (head, segment, sequence).
 template <int NS, bool GATE, bool FULL>
-__global__ void __launch_bounds__(kSsdThreads) ssd_fwd_kernel(SsdArgs a) {
+__global__ void __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+ssd_fwd_kernel(SsdArgs a) {
   constexpr int Q = kSsdQ, P = kSsdP;
-  constexpr int LDC = NS + kSsdPad;  // sC, sB, sH row stride
-  constexpr int LDX = Q + kSsdPad;   // sXt, sS row stride
-  constexpr int NCT = NS / 32;       // column tiles of the state
-  constexpr int TPW = 2 * NCT / 4;   // state tiles per wave
-  __shared__ __attribute__((aligned(16))) __bf16 sC[Q * LDC];
-  __shared__ __attribute__((aligned(16))) __bf16 sB[Q * LDC];
-  __shared__ __attribute__((aligned(16))) __bf16 sH[P * LDC];
-  __shared__ __attribute__((aligned(16))) __bf16 sXt[P * LDX];
-  __shared__ __attribute__((aligned(16))) __bf16 sS[Q * LDX];
-  __shared__ float sdt[Q], slam[Q], sw[Q];
+  constexpr int NT = NS / 16;                  // state tiles per wave
+  constexpr int NK = NS / 32;                  // k-steps over the state dimension
+  constexpr int RB = NS * 2;                   // sB / sC row bytes
+  constexpr int PPR = NS / 8;                  // 16-byte pieces per B / C row
+  constexpr int NBC = Q * PPR / kSsdThreads;   // B (and C) pieces per thread
+  constexpr int RPJ = kSsdThreads / PPR;       // rows between a thread's B / C pieces
+  constexpr int NX = Q * P / 8 / kSsdThreads;  // x pieces per thread
+  static_assert(RPJ % 8 == 0 && NX == 2, "layout");
+  __shared__ __attribute__((aligned(16))) unsigned char sB[Q * RB];
+  __shared__ __attribute__((aligned(16))) unsigned char sC[FULL ? Q * RB : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char sX[Q * P * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char sS[FULL ? Q * Q * 2 : 16];
+  __shared__ __attribute__((aligned(16))) float slam[Q], sel[Q], sw[Q], sdt[Q];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane % 32, hi8 = 8 * (lane / 32);
-  const int h = blockIdx.x;
-  const int seg = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  const int m = lane & 15, q = lane >> 4;
+  const int h = blockIdx.x, seg = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int L = a.L, H = a.H;
-  const int g = h / (H / a.G);
+  const int grp = h / (H / a.G);
   const float Ah = a.A[h];
   const float Dh = a.D ? a.D[h] : 0.0f;
   const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+  const uint32_t rowX = static_cast<uint32_t>(H) * P * 2;      // bytes per token row of x, z, out
+  const uint32_t rowBC = static_cast<uint32_t>(a.G) * NS * 2;  // bytes per token row of B, C
+  const int64_t bh = b * H + h;
 
-  // the state: tiles k = wave*TPW + i, rows p in 32*(k / NCT), columns n in 32*(k % NCT);
-  // it enters the segment from the carry (or the initial state), or from
-  // zero in the state pass
-  const size_t slot = ((static_cast<size_t>(b) * a.nseg + seg) * H + h) * P * NS;
-  const float* hin = !FULL ? nullptr : (a.nseg > 1 ? a.seg_state + slot : a.h0 ? a.h0 + (b * H + h) * P * NS : nullptr);
-  f32x16 st[TPW];
+  // ---- the state entering the segment ----
+  f32x4 st[NT];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int k = wave * TPW + i, rt = k / NCT, ct = k % NCT;
+  for (int nb = 0; nb < NT; ++nb) st[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (FULL) {
+    if (a.h0) {
+      const float* src = a.h0 + (bh * P + 16 * w + m) * NS;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int p = 32 * rt + acc_row(r, lane), n = 32 * ct + l32;
-      st[i][r] = hin ? hin[p * NS + n] : 0.0f;
+      for (int nb = 0; nb < NT; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[nb][r] = src[nmap(nb, q) + r];
     }
+    for (int j = 0; j < seg; ++j) {
+      const size_t slot = (static_cast<size_t>(b) * (a.nseg - 1) + j) * H + h;
+      float lo;
+      const float e = exp_acc(a.seg_lam[slot], lo);
+      const f32x4* hs = reinterpret_cast<const f32x4*>(a.seg_state + slot * P * NS) + w * NT * 64;
+#pragma unroll
+      for (int nb = 0; nb < NT; ++nb) {
+        const f32x4 v = hs[nb * 64 + lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[nb][r] = __builtin_fmaf(e, st[nb][r], v[r]);
+      }
+    }
+    // tiles of S above the diagonal that the products read stay zero
+    reinterpret_cast<u32x4*>(sS)[tid] = u32x4{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4*>(sS)[tid + kSsdThreads] = u32x4{0u, 0u, 0u, 0u};
   }
 
   const int nchunks = (L + Q - 1) / Q;
@@ -121,223 +254,220 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_fwd_kernel(SsdArgs a) {
   const int c_end = (c_begin + a.cps < nchunks) ? c_begin + a.cps : nchunks;
   float lam_seg = 0.0f;
 
-  // The global inputs of a chunk are fetched into registers one chunk ahead,
-  // so their latency is covered by the current chunk's work; rows past the
-  // sequence read as zeros.  x is fetched token-fastest across lanes (each
-  // lane 8 channels of one token) so that its transposed LDS copy is written
-  // without bank conflicts.
-  constexpr int VR = NS / 8;                    // 16-byte vectors per B/C row
-  constexpr int NBC = Q * VR / kSsdThreads;     // B (and C) vectors per thread
-  constexpr int NX = Q * P / 8 / kSsdThreads;   // x vectors per thread
-  uint4 pb[NBC], pc[NBC];
-  bf16x8 px[NX];
-  float pdt = 0.0f;
-  uint16_t pz[16];
-  const int yrt = wave / 2, yct = wave % 2;     // this wave's output tile
+  // per-lane offsets (loop constants)
+  const uint32_t vo_bc = (tid / PPR) * rowBC + (tid % PPR) * 16;
+  const int lds_bc = (tid / PPR) * RB + (((tid % PPR) ^ swz_bc((tid / PPR) & 7)) << 4);
+  const uint32_t vo_x = (tid >> 3) * rowX + (tid & 7) * 16;
+  const int lds_x = (tid >> 3) * 128 + (((tid & 7) ^ swz_x(tid >> 3)) << 4);
+  const uint32_t vo_y = m * rowX + (16 * w + 4 * q) * 2;  // z, out: token 16 tb + m, channels 16w+4q..+3
+  const uint32_t vo_dt = lane * static_cast<uint32_t>(H) * 2;
+  // LDS address bases of the operand reads; the loop indices (k-step, row
+  // block, tile) enter as immediate offsets
+  const int k4 = m >> 2, bq = m & 3;
+  int bc_base[2];  // B, C rows 16 blk + m, pieces 4 kk + q (kk parity kp)
+  int s_base[2];   // S rows 16 tb + m, pieces 4 kk + q
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp) {
+    bc_base[kp] = m * RB + (((4 * kp + q) ^ swz_bc(m & 7)) << 4);
+    s_base[kp] = m * 128 + (((4 * kp + q) ^ swz_s(m)) << 4);
+  }
+  const int x_ep = m * 128 + (((2 * w + (q >> 1)) ^ swz_x(m)) << 4) + 8 * (q & 1);
+  int xt_base[2];        // X^T transpose loads: rows 32 kk + 8 q + k4 + 4 f
+  int bt_base[2][2][2];  // B^T transpose loads: [f][tile pair parity][tile parity]
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int r = 8 * q + k4 + 4 * f;
+    xt_base[f] = r * 128 + (((2 * w + (bq >> 1)) ^ swz_x(r)) << 4) + 8 * (bq & 1);
+#pragma unroll
+    for (int c1 = 0; c1 < 2; ++c1)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        bt_base[f][c1][e] = r * RB + (((4 * c1 + bq) ^ swz_bc(r & 7)) << 4) + 8 * (e ^ (bq & 1));
+  }
+
+  u32x4 pb[NBC], pc[NBC], px[NX];
+  u32x2 pz[4];
+  uint32_t pdt = 0;
   auto fetch = [&](int c) {
     const int t0 = c * Q;
+    const int valid = (L - t0 < Q) ? L - t0 : Q;
+    const int64_t rbc = (b * L + t0) * a.G + grp;
+    const rsrc_t rB = make_rsrc(a.B + rbc * NS, valid * rowBC);
 #pragma unroll
-    for (int j = 0; j < NBC; ++j) {
-      const int v = tid + kSsdThreads * j;
-      const int t = v / VR, n8 = v % VR;
-      pb[j] = make_uint4(0, 0, 0, 0);
-      pc[j] = make_uint4(0, 0, 0, 0);
-      if (t0 + t < L) {
-        const size_t row = ((b * L + t0 + t) * a.G + g) * NS + 8 * n8;
-        pb[j] = *reinterpret_cast<const uint4*>(a.B + row);
-        if (FULL) pc[j] = *reinterpret_cast<const uint4*>(a.C + row);
-      }
-    }
+    for (int j = 0; j < NBC; ++j)
+      pb[j] = __builtin_amdgcn_raw_buffer_load_b128(rB, vo_bc, j * RPJ * rowBC, 0);
+    if constexpr (FULL) {
+      const rsrc_t rC = make_rsrc(a.C + rbc * NS, valid * rowBC);
 #pragma unroll
-    for (int j = 0; j < NX; ++j) {
-      const int v = tid + kSsdThreads * j;
-      const int t = v % Q, p8 = v / Q;
-      px[j] = bf16x8{};
-      if (t0 + t < L) px[j] = *reinterpret_cast<const bf16x8*>(a.x + ((b * L + t0 + t) * H + h) * P + 8 * p8);
+      for (int j = 0; j < NBC; ++j)
+        pc[j] = __builtin_amdgcn_raw_buffer_load_b128(rC, vo_bc, j * RPJ * rowBC, 0);
     }
-    if (tid < Q) {
-      pdt = 0.0f;
-      if (t0 + tid < L) {
-        const float u = to_f32(a.dt[(b * L + t0 + tid) * H + h]) + bias;
-        pdt = a.softplus ? softplus_f32(u) : u;
-      }
-    }
-    if constexpr (FULL && GATE) {
+    const int64_t rx = (b * L + t0) * H + h;
+    const rsrc_t rX = make_rsrc(a.x + rx * P, valid * rowX);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tok = t0 + 32 * yrt + acc_row(r, lane);
-        pz[r] = 0;
-        if (tok < L) pz[r] = a.z[((b * L + tok) * H + h) * P + 32 * yct + l32].bits;
-      }
-    }
+    for (int j = 0; j < NX; ++j)
+      px[j] = __builtin_amdgcn_raw_buffer_load_b128(rX, vo_x, j * 32 * rowX, 0);
+    if (w == 0)
+      pdt = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(a.dt + rx, valid * H * 2), vo_dt, 0, 0);
   };
-  if (c_begin < c_end) fetch(c_begin);
+  // the gate of a chunk is fetched after the previous chunk's outputs are written
+  auto fetch_z = [&](int c) {
+    const int t0 = c * Q;
+    const int valid = (L - t0 < Q) ? L - t0 : Q;
+    const rsrc_t rZ = make_rsrc(a.z + ((b * L + t0) * H + h) * P, valid * rowX);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+      pz[tb] = __builtin_amdgcn_raw_buffer_load_b64(rZ, vo_y, tb * 16 * rowX, 0);
+  };
+  if (c_begin < c_end) {
+    fetch(c_begin);
+    if constexpr (FULL && GATE) fetch_z(c_begin);
+  }
 
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * Q;
-    // ---- 1. stage the chunk fetched ahead, then fetch the next ----
+    // ---- 1. stage the chunk fetched ahead; wave 0 forms lambda and the weights ----
 #pragma unroll
     for (int j = 0; j < NBC; ++j) {
-      const int v = tid + kSsdThreads * j;
-      const int t = v / VR, n8 = v % VR;
-      *reinterpret_cast<uint4*>(&sB[t * LDC + 8 * n8]) = pb[j];
-      if (FULL) *reinterpret_cast<uint4*>(&sC[t * LDC + 8 * n8]) = pc[j];
+      *reinterpret_cast<u32x4*>(sB + lds_bc + j * RPJ * RB) = pb[j];
+      if constexpr (FULL) *reinterpret_cast<u32x4*>(sC + lds_bc + j * RPJ * RB) = pc[j];
     }
 #pragma unroll
-    for (int j = 0; j < NX; ++j) {
-      const int v = tid + kSsdThreads * j;
-      const int t = v % Q, p8 = v / Q;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sXt[(8 * p8 + i) * LDX + t] = px[j][i];
-    }
-    if (tid < Q) sdt[tid] = pdt;
-    uint16_t zc[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) zc[r] = pz[r];
-    if (c + 1 < c_end) fetch(c + 1);
-    __syncthreads();
-    if (wave == 0) {  // lambda: inclusive prefix sum of dt A over the chunk
-      float v = sdt[lane] * Ah;
+    for (int j = 0; j < NX; ++j) *reinterpret_cast<u32x4*>(sX + lds_x + j * 32 * 128) = px[j];
+    if (w == 0) {
+      const float u = bf_lo(pdt) + bias;
+      float dtv = a.softplus ? softplus_f32(u) : u;
+      if (t0 + lane >= L) dtv = 0.0f;  // past the end: no decay, no input
+      float v = dtv * Ah;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
-        const float u = __shfl_up(v, o);
-        if (lane >= o) v += u;
+        const float up = __shfl_up(v, o);
+        if (lane >= o) v += up;
       }
+      const float lend = __shfl(v, 63);
       slam[lane] = v;
+      sel[lane] = exp_f(v);
+      sw[lane] = dtv * exp_f(lend - v);
+      sdt[lane] = dtv;
     }
+    if (c + 1 < c_end) fetch(c + 1);
     __syncthreads();
-    const float lam_end = slam[Q - 1];
-    lam_seg += lam_end;
-    if (tid < Q) sw[tid] = sdt[tid] * exp_f(lam_end - slam[tid]);
-    if constexpr (!FULL) __syncthreads();  // (the full pass has barriers before sw is read)
+
+    // X^T operand of this wave's channels: lane (q, m) holds x[s = 32 kk + 8 q + i][16 w + m]
+    bf16x8 xa[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      xa[kk] = cat8(lds_tr(sX, xt_base[0] + 32 * 128 * kk), lds_tr(sX, xt_base[1] + 32 * 128 * kk));
 
     if constexpr (FULL) {
-    // ---- 2. S = C B^T, masked: tile (rows t in 32*(wave/2), columns s in 32*(wave%2)) ----
-    {
-      const int rt = wave / 2, ct = wave % 2;
-      f32x16 acc = {};
-#pragma unroll
-      for (int kk = 0; kk < NS / 16; ++kk) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sC[(32 * rt + l32) * LDC + 16 * kk + hi8]);
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sB[(32 * ct + l32) * LDC + 16 * kk + hi8]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+      // ---- 2. the ten non-zero tiles of S, split over the waves ----
+      if (w == 0) {
+        ssd_s_tiles<NS, 3>(sB, sC, sS, slam, sdt, bc_base, lane, 0, 0);
+      } else if (w == 1) {
+        ssd_s_tiles<NS, 3>(sB, sC, sS, slam, sdt, bc_base, lane, 1, 1);
+      } else if (w == 2) {
+        ssd_s_tiles<NS, 2>(sB, sC, sS, slam, sdt, bc_base, lane, 2, 2);
+      } else {
+        ssd_s_tiles<NS, 1>(sB, sC, sS, slam, sdt, bc_base, lane, 0, 3);
+        ssd_s_tiles<NS, 1>(sB, sC, sS, slam, sdt, bc_base, lane, 3, 3);
       }
-      const int s = 32 * ct + l32;
-      const float lam_s = slam[s], dt_s = sdt[s];
+      // bf16 copy of the entering state as the A operand of H C^T: lane (q, m)
+      // holds h[16 w + m][32 kk + 8 q + i]
+      bf16x8 hA[NK];
+      const bool odd = q & 1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * rt + acc_row(r, lane);
-        const float v = (s <= t) ? acc[r] * exp_f(slam[t] - lam_s) * dt_s : 0.0f;
-        sS[t * LDX + s] = to_bf(v);
+      for (int kk = 0; kk < NK; ++kk) {
+        const f32x4 lo = odd ? st[2 * kk + 1] : st[2 * kk];
+        const f32x4 hi = odd ? st[2 * kk] : st[2 * kk + 1];
+        const uint32_t u[4] = {pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]),
+                               pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3])};
+        hA[kk] = __builtin_bit_cast(bf16x8, u32x4{u[0], u[1], u[2], u[3]});
       }
-    }
-    // ---- 3. bf16 copy of the state entering the chunk ----
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int k = wave * TPW + i, rt = k / NCT, ct = k % NCT;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        sH[(32 * rt + acc_row(r, lane)) * LDC + 32 * ct + l32] = to_bf(st[i][r]);
-    }
-    __syncthreads();
+      __syncthreads();
 
-    // ---- 4. Y = S X + diag(e^lambda) (C h^T) + D X: tile (t in 32*(wave/2), p in 32*(wave%2)) ----
-    {
-      const int rt = wave / 2, ct = wave % 2;
-      f32x16 y1 = {}, y2 = {};
+      // ---- 3. Y^T = X^T S^T + (H C^T) diag(e^lambda) + D X^T, gated, per 16 tokens ----
+      const int64_t rx = (b * L + t0) * H + h;
+      const int valid = (L - t0 < Q) ? L - t0 : Q;
+      const rsrc_t rO = make_rsrc(a.out + rx * P, valid * rowX);
 #pragma unroll
-      for (int kk = 0; kk < Q / 16; ++kk) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sS[(32 * rt + l32) * LDX + 16 * kk + hi8]);
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sXt[(32 * ct + l32) * LDX + 16 * kk + hi8]);
-        y1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, y1, 0, 0, 0);
-      }
+      for (int tb = 0; tb < 4; ++tb) {
+        const int t = 16 * tb + m;
+        f32x4 y1 = {0.f, 0.f, 0.f, 0.f}, y2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < NS / 16; ++kk) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sC[(32 * rt + l32) * LDC + 16 * kk + hi8]);
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sH[(32 * ct + l32) * LDC + 16 * kk + hi8]);
-        y2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, y2, 0, 0, 0);
-      }
-      const int p = 32 * ct + l32;
+        for (int kk = 0; kk < (tb >= 2 ? 2 : 1); ++kk)
+          y1 = mfma16(xa[kk], lds_b128(sS, s_base[kk] + 16 * 128 * tb), y1);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * rt + acc_row(r, lane);
-        const int tok = t0 + t;
-        if (tok < L) {
-          const float xv = from_bf(sXt[p * LDX + t]);
-          float y = __builtin_fmaf(exp_f(slam[t]), y2[r], y1[r]);
-          y = __builtin_fmaf(Dh, xv, y);
-          const size_t o = ((b * L + tok) * H + h) * P + p;
-          if constexpr (GATE) y *= silu_f32(__uint_as_float(static_cast<uint32_t>(zc[r]) << 16));
-          store_act(a.out + o, y);
+        for (int kk = 0; kk < NK; ++kk)
+          y2 = mfma16(hA[kk], lds_b128(sC, bc_base[kk & 1] + 128 * (kk >> 1) + 16 * RB * tb), y2);
+        const float el = sel[t];
+        const u32x2 xr = *reinterpret_cast<const u32x2*>(sX + x_ep + 16 * 128 * tb);
+        const float xv[4] = {bf_lo(xr[0]), bf_hi(xr[0]), bf_lo(xr[1]), bf_hi(xr[1])};
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          y[r] = __builtin_fmaf(el, y2[r], y1[r]);
+          y[r] = __builtin_fmaf(Dh, xv[r], y[r]);
         }
+        if constexpr (GATE) {
+          const float zv[4] = {bf_lo(pz[tb][0]), bf_hi(pz[tb][0]), bf_lo(pz[tb][1]),
+                               bf_hi(pz[tb][1])};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[r] *= silu_f32(zv[r]);
+        }
+        const u32x2 o = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(o, rO, vo_y, tb * 16 * rowX, 0);
       }
+      if constexpr (GATE)
+        if (c + 1 < c_end) fetch_z(c + 1);
     }
-    }  // FULL
 
-    // ---- 5. h <- e^(lambda_end) h + X_w^T B ----
+    // ---- 4. h <- e^(lambda_end) h + X_w^T B ----
     {
-      const float aend = exp_f(lam_end);
+      bf16x8 xw[2];
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int k = wave * TPW + i, rt = k / NCT, ct = k % NCT;
+      for (int kk = 0; kk < 2; ++kk) {
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sw[32 * kk + 8 * q]);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sw[32 * kk + 8 * q + 4]);
+        const float f[8] = {static_cast<float>(xa[kk][0]) * w0[0], static_cast<float>(xa[kk][1]) * w0[1],
+                            static_cast<float>(xa[kk][2]) * w0[2], static_cast<float>(xa[kk][3]) * w0[3],
+                            static_cast<float>(xa[kk][4]) * w1[0], static_cast<float>(xa[kk][5]) * w1[1],
+                            static_cast<float>(xa[kk][6]) * w1[2], static_cast<float>(xa[kk][7]) * w1[3]};
+        xw[kk] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]),
+                                                   pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7])});
+      }
+      const float aend = sel[Q - 1];
+      if constexpr (!FULL) lam_seg += slam[Q - 1];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st[i][r] *= aend;
-        const int p = 32 * rt + l32, n = 32 * ct + l32;
+      for (int nb = 0; nb < NT; ++nb) {
 #pragma unroll
-        for (int kk = 0; kk < Q / 16; ++kk) {
-          const int s0 = 16 * kk + hi8;
-          const bf16x8 xv = *reinterpret_cast<const bf16x8*>(&sXt[p * LDX + s0]);
-          bf16x8 av, bv;
+        for (int r = 0; r < 4; ++r) st[nb][r] *= aend;
+        const int c = nb >> 1, c1 = c & 1, e = nb & 1;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            av[j] = to_bf(from_bf(xv[j]) * sw[s0 + j]);
-            bv[j] = sB[(s0 + j) * LDC + n];
-          }
-          st[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, st[i], 0, 0, 0);
+        for (int kk = 0; kk < 2; ++kk) {
+          const int imm = 32 * RB * kk + 128 * (c >> 1);
+          const s16x4 v0 = lds_tr(sB, bt_base[0][c1][e] + imm);
+          const s16x4 v1 = lds_tr(sB, bt_base[1][c1][e] + imm);
+          st[nb] = mfma16(cat8(v0, v1), xw[kk], st[nb]);
         }
       }
     }
     __syncthreads();  // the next chunk restages every LDS buffer
   }
 
-  // the state pass leaves its segment's end state; the full pass of the
-  // last segment leaves the final state
-  float* dst = !FULL ? a.seg_state + slot
-                     : (seg == a.nseg - 1 && a.last_state ? a.last_state + (b * H + h) * P * NS
-                                                          : nullptr);
-  if (dst) {
+  if constexpr (FULL) {
+    if (seg == a.nseg - 1 && a.last_state) {
+      float* dst = a.last_state + (bh * P + 16 * w + m) * NS;
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int k = wave * TPW + i, rt = k / NCT, ct = k % NCT;
+      for (int nb = 0; nb < NT; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int p = 32 * rt + acc_row(r, lane), n = 32 * ct + l32;
-        dst[p * NS + n] = st[i][r];
-      }
+        for (int r = 0; r < 4; ++r) dst[nmap(nb, q) + r] = st[nb][r];
     }
-  }
-  if (!FULL && tid == 0) a.seg_lam[(static_cast<size_t>(b) * a.nseg + seg) * H + h] = lam_seg;
-}
-
-// Carry over segments: one lane per (sequence, head, p, n).  h runs from the
-// initial state through the segments' end states, h <- e^(lambda_s) h + H_s,
-// and each slot is overwritten with the state entering that segment.
-__global__ void __launch_bounds__(256) ssd_carry_kernel(SsdArgs a, int PN) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t per_b = static_cast<int64_t>(a.H) * PN;
-  if (idx >= per_b) return;
-  const int64_t b = blockIdx.y;
-  const int h = static_cast<int>(idx / PN);
-  const int e = static_cast<int>(idx % PN);
-  float hv = a.h0 ? a.h0[(b * a.H + h) * PN + e] : 0.0f;
-  for (int s = 0; s < a.nseg; ++s) {
-    float* sp = a.seg_state + ((b * a.nseg + s) * a.H + h) * static_cast<int64_t>(PN) + e;
-    const float Hs = (s < a.nseg - 1) ? *sp : 0.0f;
-    *sp = hv;
-    if (s < a.nseg - 1) {
-      float unused;
-      hv = __builtin_fmaf(exp_acc(a.seg_lam[(b * a.nseg + s) * a.H + h], unused), hv, Hs);
-    }
+  } else {
+    const size_t slot = (static_cast<size_t>(b) * (a.nseg - 1) + seg) * H + h;
+    f32x4* hs = reinterpret_cast<f32x4*>(a.seg_state + slot * P * NS) + w * NT * 64;
+#pragma unroll
+    for (int nb = 0; nb < NT; ++nb) hs[nb * 64 + lane] = st[nb];
+    if (tid == 0) a.seg_lam[slot] = lam_seg;
   }
 }
 
@@ -345,11 +475,11 @@ struct SsdPlan {
   int cps, nseg;
 };
 
-// Segments: enough (head, segment, sequence) workgroups for about four per
-// compute unit, at least two chunks per segment.
+// Segments: enough (head, segment, sequence) workgroups for the resident
+// workgroups of every compute unit, at least two chunks per segment.
 SsdPlan plan_ssd(int64_t batch, int64_t L, int64_t H) {
   const int64_t nchunks = (L + kSsdQ - 1) / kSsdQ;
-  const int64_t target = 4LL * device_cus();
+  const int64_t target = static_cast<int64_t>(SSM_SSD_WG_PER_CU) * device_cus();
   int64_t nseg = (target + batch * H - 1) / (batch * H);
   if (nseg > nchunks / 2) nseg = nchunks / 2;
   if (nseg < 1) nseg = 1;
@@ -361,8 +491,8 @@ SsdPlan plan_ssd(int64_t batch, int64_t L, int64_t H) {
 
 size_t ssd_workspace(int64_t batch, int64_t H, int64_t P, int64_t N, const SsdPlan& p) {
   if (p.nseg <= 1) return 0;
-  const size_t states = static_cast<size_t>(batch) * p.nseg * H * P * N * 4;
-  return (states + 255) / 256 * 256 + static_cast<size_t>(batch) * p.nseg * H * 4;
+  const size_t states = static_cast<size_t>(batch) * (p.nseg - 1) * H * P * N * 4;
+  return (states + 255) / 256 * 256 + static_cast<size_t>(batch) * (p.nseg - 1) * H * 4;
 }
 
 }  // namespace ssm
@@ -403,7 +533,7 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* dt_bias, int dt_soft
   if (seqlen > 0 && (!x || !dt || !B || !C || !out))
     return fail(SSM_ERR_NULL, "%s: x, dt, B, C and out are required", fn);
   const struct { const void* p; size_t k; const char* n; } al[] = {
-      {x, 16, "x"}, {B, 16, "B"}, {C, 16, "C"}, {dt, 2, "dt"}, {z, 2, "z"}, {out, 2, "out"},
+      {x, 16, "x"}, {B, 16, "B"}, {C, 16, "C"}, {dt, 2, "dt"}, {z, 8, "z"}, {out, 8, "out"},
       {A, 4, "A"}, {D, 4, "D"}, {dt_bias, 4, "dt_bias"}, {last_state, 4, "last_state"},
       {initial_state, 4, "initial_state"}};
   for (const auto& e : al)
@@ -438,7 +568,7 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* dt_bias, int dt_soft
   for (const auto& o : outs)
     if (overlap(wsp, o)) return fail(SSM_ERR_ALIAS, "%s: workspace overlaps output %s", fn, o.name);
   if (seqlen == 0 && !last_state) return SSM_OK;
-  const size_t sbytes = static_cast<size_t>(batch) * plan.nseg * nheads * headdim * dstate * 4;
+  const size_t sbytes = static_cast<size_t>(batch) * (plan.nseg - 1) * nheads * headdim * dstate * 4;
   float* seg_state = need ? static_cast<float*>(workspace) : nullptr;
   float* seg_lam = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                    (sbytes + 255) / 256 * 256)
@@ -452,16 +582,11 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* dt_bias, int dt_soft
   const dim3 block(kSsdThreads);
   const bool big = dstate == 128;
   if (plan.nseg > 1) {
-    // state pass over every segment but the last, then the carry
+    // state pass over every segment but the last
     const dim3 g1(static_cast<unsigned>(nheads), static_cast<unsigned>(plan.nseg - 1),
                   static_cast<unsigned>(batch));
     if (big) hipLaunchKernelGGL((ssd_fwd_kernel<128, false, false>), g1, block, 0, stream, args);
     else hipLaunchKernelGGL((ssd_fwd_kernel<64, false, false>), g1, block, 0, stream, args);
-    const int PN = static_cast<int>(headdim * dstate);
-    const int64_t lanes = nheads * PN;
-    hipLaunchKernelGGL(ssd_carry_kernel,
-                       dim3(static_cast<unsigned>((lanes + 255) / 256), static_cast<unsigned>(batch)),
-                       dim3(256), 0, stream, args, PN);
   }
   const dim3 grid(static_cast<unsigned>(nheads), static_cast<unsigned>(plan.nseg),
                   static_cast<unsigned>(batch));
