@@ -69,8 +69,11 @@ constexpr int kSsdQ = 64;         // chunk length (tokens)
 constexpr int kSsdP = 64;         // head dimension
 constexpr int kSsdThreads = 256;  // 4 waves
 
+#ifndef SSM_SSD_FORCE_NSEG
+#define SSM_SSD_FORCE_NSEG 0  // a fixed number of segments (0: from the device size)
+#endif
 #ifndef SSM_SSD_WG_PER_CU
-#define SSM_SSD_WG_PER_CU 3  // workgroups per compute unit the segment plan aims for
+#define SSM_SSD_WG_PER_CU 4  // workgroups per compute unit the segment plan aims for
 #endif
 
 struct SsdArgs {
@@ -97,6 +100,25 @@ struct SsdArgs {
 };
 
 __device__ __forceinline__ float exp_f(float v) { return __builtin_amdgcn_exp2f(v * kLog2e); }
+
+// v shifted across lanes by a DPP pattern; lanes without a source read 0
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, false));
+}
+
+// inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8
+// inside each row of 16, then the row totals (row_bcast15 to rows 1 and 3,
+// row_bcast31 to rows 2 and 3)
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v += dpp_or_zero<0x111, 0xf>(v);
+  v += dpp_or_zero<0x112, 0xf>(v);
+  v += dpp_or_zero<0x114, 0xf>(v);
+  v += dpp_or_zero<0x118, 0xf>(v);
+  v += dpp_or_zero<0x142, 0xa>(v);
+  v += dpp_or_zero<0x143, 0xc>(v);
+  return v;
+}
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -139,7 +161,11 @@ __device__ __forceinline__ int swz_s(int r) { return r & 7; }
 // State tile nb of a wave holds h^T rows n = nmap(nb, q) + r for the lanes
 // of group q (accumulator elements r = 0..3): the two tiles 2i, 2i+1 of a
 // group cover the eight consecutive n = 32i + 8q .. +7, the lower four in
-// tile 2i for even q and in tile 2i+1 for odd q.
+// tile 2i for even q and in tile 2i+1 for odd q.  B and C rows hold the
+// 8-byte halves of odd 16-byte pieces swapped, so the k-step order of the
+// readout H C^T (tile 2i's values first) matches C's 16-byte row reads
+// without a per-lane select, and the transpose loads of B^T for tile nb
+// read half nb % 2 of every piece.
 __device__ __forceinline__ int nmap(int nb, int q) {
   return 32 * (nb >> 1) + 8 * q + 4 * ((nb & 1) ^ (q & 1));
 }
@@ -176,7 +202,7 @@ __device__ __forceinline__ void ssd_s_tiles(const unsigned char* sB, const unsig
     float v[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float e = acc[i][r] * exp_f(lt - ls[r]) * ds[r];
+      const float e = acc[i][r] * __builtin_amdgcn_exp2f(lt - ls[r]) * ds[r];
       v[r] = (tb > sb || 4 * q + r <= m) ? e : 0.0f;
     }
     const u32x2 pk = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
@@ -204,7 +230,7 @@ ssd_fwd_kernel(SsdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char sC[FULL ? Q * RB : 16];
   __shared__ __attribute__((aligned(16))) unsigned char sX[Q * P * 2];
   __shared__ __attribute__((aligned(16))) unsigned char sS[FULL ? Q * Q * 2 : 16];
-  __shared__ __attribute__((aligned(16))) float slam[Q], sel[Q], sw[Q], sdt[Q];
+  __shared__ __attribute__((aligned(16))) float slam[Q], sel[Q], sw[Q], sdt[Q];  // slam: lambda log2(e)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -256,7 +282,10 @@ ssd_fwd_kernel(SsdArgs a) {
 
   // per-lane offsets (loop constants)
   const uint32_t vo_bc = (tid / PPR) * rowBC + (tid % PPR) * 16;
+  // B and C rows: the two 8-byte halves of every odd 16-byte piece are
+  // stored swapped (see the state tiles' n mapping)
   const int lds_bc = (tid / PPR) * RB + (((tid % PPR) ^ swz_bc((tid / PPR) & 7)) << 4);
+  const int lds_bc_lo = lds_bc + 8 * (tid & 1), lds_bc_hi = lds_bc + 8 * (1 - (tid & 1));
   const uint32_t vo_x = (tid >> 3) * rowX + (tid & 7) * 16;
   const int lds_x = (tid >> 3) * 128 + (((tid & 7) ^ swz_x(tid >> 3)) << 4);
   const uint32_t vo_y = m * rowX + (16 * w + 4 * q) * 2;  // z, out: token 16 tb + m, channels 16w+4q..+3
@@ -282,15 +311,25 @@ ssd_fwd_kernel(SsdArgs a) {
     for (int c1 = 0; c1 < 2; ++c1)
 #pragma unroll
       for (int e = 0; e < 2; ++e)
-        bt_base[f][c1][e] = r * RB + (((4 * c1 + bq) ^ swz_bc(r & 7)) << 4) + 8 * (e ^ (bq & 1));
+        bt_base[f][c1][e] = r * RB + (((4 * c1 + bq) ^ swz_bc(r & 7)) << 4) + 8 * e;
   }
 
   u32x4 pb[NBC], pc[NBC], px[NX];
   u32x2 pz[4];
   uint32_t pdt = 0;
+  // Every global access of the chunk loop is issued unconditionally, so the
+  // compiler's counts of outstanding loads are exact and a wait for one
+  // chunk's data never drains the next chunk's prefetch; a chunk outside the
+  // segment gets a descriptor of zero bytes (its loads read zero and touch
+  // no memory).
+  auto rows_of = [&](int c) {
+    const int t0 = c * Q;
+    const int v = (L - t0 < Q) ? L - t0 : Q;
+    return (c < c_end && v > 0) ? v : 0;
+  };
   auto fetch = [&](int c) {
     const int t0 = c * Q;
-    const int valid = (L - t0 < Q) ? L - t0 : Q;
+    const int valid = rows_of(c);
     const int64_t rbc = (b * L + t0) * a.G + grp;
     const rsrc_t rB = make_rsrc(a.B + rbc * NS, valid * rowBC);
 #pragma unroll
@@ -307,13 +346,14 @@ ssd_fwd_kernel(SsdArgs a) {
 #pragma unroll
     for (int j = 0; j < NX; ++j)
       px[j] = __builtin_amdgcn_raw_buffer_load_b128(rX, vo_x, j * 32 * rowX, 0);
-    if (w == 0)
-      pdt = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(a.dt + rx, valid * H * 2), vo_dt, 0, 0);
+    // (only wave 0 uses dt: the other waves' descriptor has no bytes)
+    pdt = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(a.dt + rx, w == 0 ? valid * H * 2 : 0),
+                                               vo_dt, 0, 0);
   };
   // the gate of a chunk is fetched after the previous chunk's outputs are written
   auto fetch_z = [&](int c) {
     const int t0 = c * Q;
-    const int valid = (L - t0 < Q) ? L - t0 : Q;
+    const int valid = rows_of(c);
     const rsrc_t rZ = make_rsrc(a.z + ((b * L + t0) * H + h) * P, valid * rowX);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
@@ -329,8 +369,13 @@ ssd_fwd_kernel(SsdArgs a) {
     // ---- 1. stage the chunk fetched ahead; wave 0 forms lambda and the weights ----
 #pragma unroll
     for (int j = 0; j < NBC; ++j) {
-      *reinterpret_cast<u32x4*>(sB + lds_bc + j * RPJ * RB) = pb[j];
-      if constexpr (FULL) *reinterpret_cast<u32x4*>(sC + lds_bc + j * RPJ * RB) = pc[j];
+      const int o = j * RPJ * RB;
+      *reinterpret_cast<u32x2*>(sB + lds_bc_lo + o) = u32x2{pb[j][0], pb[j][1]};
+      *reinterpret_cast<u32x2*>(sB + lds_bc_hi + o) = u32x2{pb[j][2], pb[j][3]};
+      if constexpr (FULL) {
+        *reinterpret_cast<u32x2*>(sC + lds_bc_lo + o) = u32x2{pc[j][0], pc[j][1]};
+        *reinterpret_cast<u32x2*>(sC + lds_bc_hi + o) = u32x2{pc[j][2], pc[j][3]};
+      }
     }
 #pragma unroll
     for (int j = 0; j < NX; ++j) *reinterpret_cast<u32x4*>(sX + lds_x + j * 32 * 128) = px[j];
@@ -338,19 +383,15 @@ ssd_fwd_kernel(SsdArgs a) {
       const float u = bf_lo(pdt) + bias;
       float dtv = a.softplus ? softplus_f32(u) : u;
       if (t0 + lane >= L) dtv = 0.0f;  // past the end: no decay, no input
-      float v = dtv * Ah;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float up = __shfl_up(v, o);
-        if (lane >= o) v += up;
-      }
-      const float lend = __shfl(v, 63);
+      // lambda in log2 units: exponentials below are exp2 of differences
+      const float v = wave_prefix_sum(dtv * (Ah * kLog2e));
+      const float lend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
       slam[lane] = v;
-      sel[lane] = exp_f(v);
-      sw[lane] = dtv * exp_f(lend - v);
+      sel[lane] = __builtin_amdgcn_exp2f(v);
+      sw[lane] = dtv * __builtin_amdgcn_exp2f(lend - v);
       sdt[lane] = dtv;
     }
-    if (c + 1 < c_end) fetch(c + 1);
+    fetch(c + 1);
     __syncthreads();
 
     // X^T operand of this wave's channels: lane (q, m) holds x[s = 32 kk + 8 q + i][16 w + m]
@@ -372,16 +413,13 @@ ssd_fwd_kernel(SsdArgs a) {
         ssd_s_tiles<NS, 1>(sB, sC, sS, slam, sdt, bc_base, lane, 3, 3);
       }
       // bf16 copy of the entering state as the A operand of H C^T: lane (q, m)
-      // holds h[16 w + m][32 kk + 8 q + i]
+      // holds h[16 w + m][n] for the n of its tiles 2 kk, 2 kk + 1 in that order
       bf16x8 hA[NK];
-      const bool odd = q & 1;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const f32x4 lo = odd ? st[2 * kk + 1] : st[2 * kk];
-        const f32x4 hi = odd ? st[2 * kk] : st[2 * kk + 1];
-        const uint32_t u[4] = {pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]),
-                               pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3])};
-        hA[kk] = __builtin_bit_cast(bf16x8, u32x4{u[0], u[1], u[2], u[3]});
+        const f32x4 lo = st[2 * kk], hi = st[2 * kk + 1];
+        hA[kk] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]),
+                                                   pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3])});
       }
       __syncthreads();
 
@@ -417,8 +455,7 @@ ssd_fwd_kernel(SsdArgs a) {
         const u32x2 o = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
         __builtin_amdgcn_raw_buffer_store_b64(o, rO, vo_y, tb * 16 * rowX, 0);
       }
-      if constexpr (GATE)
-        if (c + 1 < c_end) fetch_z(c + 1);
+      if constexpr (GATE) fetch_z(c + 1);
     }
 
     // ---- 4. h <- e^(lambda_end) h + X_w^T B ----
@@ -436,7 +473,7 @@ ssd_fwd_kernel(SsdArgs a) {
                                                    pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7])});
       }
       const float aend = sel[Q - 1];
-      if constexpr (!FULL) lam_seg += slam[Q - 1];
+      if constexpr (!FULL) lam_seg += slam[Q - 1] * kLn2;
 #pragma unroll
       for (int nb = 0; nb < NT; ++nb) {
 #pragma unroll
@@ -481,6 +518,7 @@ SsdPlan plan_ssd(int64_t batch, int64_t L, int64_t H) {
   const int64_t nchunks = (L + kSsdQ - 1) / kSsdQ;
   const int64_t target = static_cast<int64_t>(SSM_SSD_WG_PER_CU) * device_cus();
   int64_t nseg = (target + batch * H - 1) / (batch * H);
+  if (SSM_SSD_FORCE_NSEG > 0) nseg = SSM_SSD_FORCE_NSEG;
   if (nseg > nchunks / 2) nseg = nchunks / 2;
   if (nseg < 1) nseg = 1;
   int64_t cps = (nchunks + nseg - 1) / nseg;
