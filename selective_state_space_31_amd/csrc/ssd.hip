@@ -211,6 +211,14 @@ __device__ __forceinline__ void ssd_s_tiles(const unsigned char* sB, const unsig
   }
 }
 
+// Zero tile (sb, tb), sb > tb, of S: above the diagonal, read by the products
+// of the k-steps that straddle the diagonal.
+__device__ __forceinline__ void ssd_s_zero(unsigned char* sS, int lane, int sb, int tb) {
+  const int m = lane & 15, q = lane >> 4, t = 16 * tb + m;
+  *reinterpret_cast<u32x2*>(sS + t * 128 + (((2 * sb + (q >> 1)) ^ swz_s(t)) << 4) + 8 * (q & 1)) =
+      u32x2{0u, 0u};
+}
+
 // FULL: outputs (and the last segment's final state); otherwise the state
 // pass: only the state update, from zero, leaving the segment's end state
 // and total log-decay.  Block (head, segment, sequence).
@@ -227,9 +235,14 @@ ssd_fwd_kernel(SsdArgs a) {
   constexpr int NX = Q * P / 8 / kSsdThreads;  // x pieces per thread
   static_assert(RPJ % 8 == 0 && NX == 2, "layout");
   __shared__ __attribute__((aligned(16))) unsigned char sB[Q * RB];
-  __shared__ __attribute__((aligned(16))) unsigned char sC[FULL ? Q * RB : 16];
+  // C and S share one region: once every wave has formed its products, the
+  // region holds the float32 outputs before the gate (Q x P x 4 bytes)
+  static_assert(Q * RB + Q * Q * 2 >= Q * P * 4, "output staging fits");
+  __shared__ __attribute__((aligned(16))) unsigned char sCS[FULL ? Q * RB + Q * Q * 2 : 16];
   __shared__ __attribute__((aligned(16))) unsigned char sX[Q * P * 2];
-  __shared__ __attribute__((aligned(16))) unsigned char sS[FULL ? Q * Q * 2 : 16];
+  unsigned char* const sC = sCS;
+  unsigned char* const sS = sCS + (FULL ? Q * RB : 0);
+  unsigned char* const sY = sCS;
   __shared__ __attribute__((aligned(16))) float slam[Q], sel[Q], sw[Q], sdt[Q];  // slam: lambda log2(e)
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -270,9 +283,6 @@ ssd_fwd_kernel(SsdArgs a) {
         for (int r = 0; r < 4; ++r) st[nb][r] = __builtin_fmaf(e, st[nb][r], v[r]);
       }
     }
-    // tiles of S above the diagonal that the products read stay zero
-    reinterpret_cast<u32x4*>(sS)[tid] = u32x4{0u, 0u, 0u, 0u};
-    reinterpret_cast<u32x4*>(sS)[tid + kSsdThreads] = u32x4{0u, 0u, 0u, 0u};
   }
 
   const int nchunks = (L + Q - 1) / Q;
@@ -288,7 +298,8 @@ ssd_fwd_kernel(SsdArgs a) {
   const int lds_bc_lo = lds_bc + 8 * (tid & 1), lds_bc_hi = lds_bc + 8 * (1 - (tid & 1));
   const uint32_t vo_x = (tid >> 3) * rowX + (tid & 7) * 16;
   const int lds_x = (tid >> 3) * 128 + (((tid & 7) ^ swz_x(tid >> 3)) << 4);
-  const uint32_t vo_y = m * rowX + (16 * w + 4 * q) * 2;  // z, out: token 16 tb + m, channels 16w+4q..+3
+  // z, out: whole 128-byte rows; lane -> token 16 w + 8 i + lane / 8, channels 8 (lane % 8) .. +7
+  const uint32_t vo_r = (lane >> 3) * rowX + (lane & 7) * 16;
   const uint32_t vo_dt = lane * static_cast<uint32_t>(H) * 2;
   // LDS address bases of the operand reads; the loop indices (k-step, row
   // block, tile) enter as immediate offsets
@@ -302,20 +313,17 @@ ssd_fwd_kernel(SsdArgs a) {
   }
   const int x_ep = m * 128 + (((2 * w + (q >> 1)) ^ swz_x(m)) << 4) + 8 * (q & 1);
   int xt_base[2];        // X^T transpose loads: rows 32 kk + 8 q + k4 + 4 f
-  int bt_base[2][2][2];  // B^T transpose loads: [f][tile pair parity][tile parity]
+  int bt_base[2][2];     // B^T transpose loads: [f][tile pair parity]
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     const int r = 8 * q + k4 + 4 * f;
     xt_base[f] = r * 128 + (((2 * w + (bq >> 1)) ^ swz_x(r)) << 4) + 8 * (bq & 1);
 #pragma unroll
-    for (int c1 = 0; c1 < 2; ++c1)
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        bt_base[f][c1][e] = r * RB + (((4 * c1 + bq) ^ swz_bc(r & 7)) << 4) + 8 * e;
+    for (int c1 = 0; c1 < 2; ++c1) bt_base[f][c1] = r * RB + (((4 * c1 + bq) ^ swz_bc(r & 7)) << 4);
   }
 
   u32x4 pb[NBC], pc[NBC], px[NX];
-  u32x2 pz[4];
+  u32x4 pz[2];
   uint32_t pdt = 0;
   // Every global access of the chunk loop is issued unconditionally, so the
   // compiler's counts of outstanding loads are exact and a wait for one
@@ -327,10 +335,11 @@ ssd_fwd_kernel(SsdArgs a) {
     const int v = (L - t0 < Q) ? L - t0 : Q;
     return (c < c_end && v > 0) ? v : 0;
   };
-  auto fetch = [&](int c) {
-    const int t0 = c * Q;
+  // B and C (shared by the heads of a group, mostly served by L2) are
+  // fetched after the current chunk's readout, x and dt one whole chunk ahead
+  auto fetch_bc = [&](int c) {
     const int valid = rows_of(c);
-    const int64_t rbc = (b * L + t0) * a.G + grp;
+    const int64_t rbc = (b * L + c * Q) * a.G + grp;
     const rsrc_t rB = make_rsrc(a.B + rbc * NS, valid * rowBC);
 #pragma unroll
     for (int j = 0; j < NBC; ++j)
@@ -341,7 +350,10 @@ ssd_fwd_kernel(SsdArgs a) {
       for (int j = 0; j < NBC; ++j)
         pc[j] = __builtin_amdgcn_raw_buffer_load_b128(rC, vo_bc, j * RPJ * rowBC, 0);
     }
-    const int64_t rx = (b * L + t0) * H + h;
+  };
+  auto fetch_x = [&](int c) {
+    const int valid = rows_of(c);
+    const int64_t rx = (b * L + c * Q) * H + h;
     const rsrc_t rX = make_rsrc(a.x + rx * P, valid * rowX);
 #pragma unroll
     for (int j = 0; j < NX; ++j)
@@ -356,11 +368,12 @@ ssd_fwd_kernel(SsdArgs a) {
     const int valid = rows_of(c);
     const rsrc_t rZ = make_rsrc(a.z + ((b * L + t0) * H + h) * P, valid * rowX);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-      pz[tb] = __builtin_amdgcn_raw_buffer_load_b64(rZ, vo_y, tb * 16 * rowX, 0);
+    for (int i = 0; i < 2; ++i)
+      pz[i] = __builtin_amdgcn_raw_buffer_load_b128(rZ, vo_r, (16 * w + 8 * i) * rowX, 0);
   };
   if (c_begin < c_end) {
-    fetch(c_begin);
+    fetch_bc(c_begin);
+    fetch_x(c_begin);
     if constexpr (FULL && GATE) fetch_z(c_begin);
   }
 
@@ -391,7 +404,8 @@ ssd_fwd_kernel(SsdArgs a) {
       sw[lane] = dtv * __builtin_amdgcn_exp2f(lend - v);
       sdt[lane] = dtv;
     }
-    fetch(c + 1);
+    fetch_x(c + 1);
+    if constexpr (!FULL) fetch_bc(c + 1);
     __syncthreads();
 
     // X^T operand of this wave's channels: lane (q, m) holds x[s = 32 kk + 8 q + i][16 w + m]
@@ -402,12 +416,16 @@ ssd_fwd_kernel(SsdArgs a) {
 
     if constexpr (FULL) {
       // ---- 2. the ten non-zero tiles of S, split over the waves ----
+      // (the two zero tiles are rewritten every chunk: the outputs staged
+      // at the end of a chunk may cover S)
       if (w == 0) {
         ssd_s_tiles<NS, 3>(sB, sC, sS, slam, sdt, bc_base, lane, 0, 0);
+        ssd_s_zero(sS, lane, 1, 0);
       } else if (w == 1) {
         ssd_s_tiles<NS, 3>(sB, sC, sS, slam, sdt, bc_base, lane, 1, 1);
       } else if (w == 2) {
         ssd_s_tiles<NS, 2>(sB, sC, sS, slam, sdt, bc_base, lane, 2, 2);
+        ssd_s_zero(sS, lane, 3, 2);
       } else {
         ssd_s_tiles<NS, 1>(sB, sC, sS, slam, sdt, bc_base, lane, 0, 3);
         ssd_s_tiles<NS, 1>(sB, sC, sS, slam, sdt, bc_base, lane, 3, 3);
@@ -423,39 +441,46 @@ ssd_fwd_kernel(SsdArgs a) {
       }
       __syncthreads();
 
-      // ---- 3. Y^T = X^T S^T + (H C^T) diag(e^lambda) + D X^T, gated, per 16 tokens ----
-      const int64_t rx = (b * L + t0) * H + h;
-      const int valid = (L - t0 < Q) ? L - t0 : Q;
-      const rsrc_t rO = make_rsrc(a.out + rx * P, valid * rowX);
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const int t = 16 * tb + m;
-        f32x4 y1 = {0.f, 0.f, 0.f, 0.f}, y2 = {0.f, 0.f, 0.f, 0.f};
+      // ---- 3. Y^T = X^T S^T + (H C^T) diag(e^lambda) + D X^T, per 16 tokens ----
+      // products of token block tb (the masked intra-chunk part and the readout)
+      auto products = [&](int tb, f32x4& y1, f32x4& y2) {
+        y1 = f32x4{0.f, 0.f, 0.f, 0.f};
+        y2 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < (tb >= 2 ? 2 : 1); ++kk)
           y1 = mfma16(xa[kk], lds_b128(sS, s_base[kk] + 16 * 128 * tb), y1);
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk)
           y2 = mfma16(hA[kk], lds_b128(sC, bc_base[kk & 1] + 128 * (kk >> 1) + 16 * RB * tb), y2);
-        const float el = sel[t];
+      };
+      // y before the gate: lane (q, m) holds channels 16 w + 4 q .. +3 of token 16 tb + m
+      auto combine = [&](int tb, const f32x4& y1, const f32x4& y2) {
+        const float el = sel[16 * tb + m];
         const u32x2 xr = *reinterpret_cast<const u32x2*>(sX + x_ep + 16 * 128 * tb);
         const float xv[4] = {bf_lo(xr[0]), bf_hi(xr[0]), bf_lo(xr[1]), bf_hi(xr[1])};
-        float y[4];
+        f32x4 y;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          y[r] = __builtin_fmaf(el, y2[r], y1[r]);
-          y[r] = __builtin_fmaf(Dh, xv[r], y[r]);
-        }
-        if constexpr (GATE) {
-          const float zv[4] = {bf_lo(pz[tb][0]), bf_hi(pz[tb][0]), bf_lo(pz[tb][1]),
-                               bf_hi(pz[tb][1])};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) y[r] *= silu_f32(zv[r]);
-        }
-        const u32x2 o = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(o, rO, vo_y, tb * 16 * rowX, 0);
+        for (int r = 0; r < 4; ++r) y[r] = __builtin_fmaf(Dh, xv[r], __builtin_fmaf(el, y2[r], y1[r]));
+        return y;
+      };
+      f32x4 yp[4];
+      {
+        f32x4 ya1, ya2, yb1, yb2;
+        products(0, ya1, ya2);
+        products(1, yb1, yb2);
+        yp[0] = combine(0, ya1, ya2);
+        products(2, ya1, ya2);
+        yp[1] = combine(1, yb1, yb2);
+        products(3, yb1, yb2);
+        yp[2] = combine(2, ya1, ya2);
+        yp[3] = combine(3, yb1, yb2);
       }
-      if constexpr (GATE) fetch_z(c + 1);
+      __syncthreads();  // every wave is done with C and S
+      // float32 rows of 64 channels, 16-byte pieces swizzled by token % 16
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        *reinterpret_cast<f32x4*>(sY + (16 * tb + m) * 256 + (((4 * w + q) ^ m) << 4)) = yp[tb];
+      fetch_bc(c + 1);
     }
 
     // ---- 4. h <- e^(lambda_end) h + X_w^T B ----
@@ -474,19 +499,49 @@ ssd_fwd_kernel(SsdArgs a) {
       }
       const float aend = sel[Q - 1];
       if constexpr (!FULL) lam_seg += slam[Q - 1] * kLn2;
+      // A operands (B^T) of tile nb for both k-steps, read one tile ahead
+      auto bt_read = [&](int nb, int kk) {
+        const int imm = 32 * RB * kk + 128 * (nb >> 2) + 8 * (nb & 1);
+        const int c1 = (nb >> 1) & 1;
+        return cat8(lds_tr(sB, bt_base[0][c1] + imm), lds_tr(sB, bt_base[1][c1] + imm));
+      };
+      bf16x8 an0 = bt_read(0, 0), an1 = bt_read(0, 1);
 #pragma unroll
       for (int nb = 0; nb < NT; ++nb) {
+        const bf16x8 a0 = an0, a1 = an1;
+        if (nb + 1 < NT) {
+          an0 = bt_read(nb + 1, 0);
+          an1 = bt_read(nb + 1, 1);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) st[nb][r] *= aend;
-        const int c = nb >> 1, c1 = c & 1, e = nb & 1;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int imm = 32 * RB * kk + 128 * (c >> 1);
-          const s16x4 v0 = lds_tr(sB, bt_base[0][c1][e] + imm);
-          const s16x4 v1 = lds_tr(sB, bt_base[1][c1][e] + imm);
-          st[nb] = mfma16(cat8(v0, v1), xw[kk], st[nb]);
-        }
+        st[nb] = mfma16(a0, xw[0], st[nb]);
+        st[nb] = mfma16(a1, xw[1], st[nb]);
       }
+    }
+    if constexpr (FULL) {
+      __syncthreads();  // the outputs before the gate are complete
+      // ---- 5. gate and store: wave w writes tokens 16 w .. 16 w + 15, whole rows ----
+      const int valid = (L - t0 < Q) ? L - t0 : Q;
+      const rsrc_t rO = make_rsrc(a.out + ((b * L + t0) * H + h) * P, valid * rowX);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int t = 16 * w + 8 * i + (lane >> 3), pc0 = 2 * (lane & 7);
+        const f32x4 u0 = *reinterpret_cast<const f32x4*>(sY + t * 256 + ((pc0 ^ (t & 15)) << 4));
+        const f32x4 u1 = *reinterpret_cast<const f32x4*>(sY + t * 256 + (((pc0 + 1) ^ (t & 15)) << 4));
+        float y[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+        if constexpr (GATE) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            y[2 * j] *= silu_f32(bf_lo(pz[i][j]));
+            y[2 * j + 1] *= silu_f32(bf_hi(pz[i][j]));
+          }
+        }
+        const u32x4 o = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
+                         pack_bf16(y[6], y[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(o, rO, vo_r, (16 * w + 8 * i) * rowX, 0);
+      }
+      if constexpr (GATE) fetch_z(c + 1);
     }
     __syncthreads();  // the next chunk restages every LDS buffer
   }
