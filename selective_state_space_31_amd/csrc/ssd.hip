@@ -330,10 +330,13 @@ ssd_fwd_kernel(SsdArgs a) {
   // chunk's data never drains the next chunk's prefetch; a chunk outside the
   // segment gets a descriptor of zero bytes (its loads read zero and touch
   // no memory).
+  // (the clamp is taken back to a scalar register: descriptors are scalar,
+  // and a count the compiler leaves in a vector register would wrap every
+  // load in a loop over lanes)
   auto rows_of = [&](int c) {
     const int t0 = c * Q;
     const int v = (L - t0 < Q) ? L - t0 : Q;
-    return (c < c_end && v > 0) ? v : 0;
+    return __builtin_amdgcn_readfirstlane((c < c_end && v > 0) ? v : 0);
   };
   // B and C (shared by the heads of a group, mostly served by L2) are
   // fetched after the current chunk's readout, x and dt one whole chunk ahead
