@@ -44,8 +44,11 @@ namespace ssm {
                                                       hipStream_t);
 SSM_BWD_STATE_INSTANCES(SSM_EXTERN_STATES)
 
+#ifndef SSM_BWD_MAX_SUB
+#define SSM_BWD_MAX_SUB 2  // sub-chunks per stripe at most
+#endif
 constexpr int kBwdSub = 16;        // tokens per recomputed sub-chunk
-constexpr int kBwdMaxSub = 8;      // sub-chunks per stripe
+constexpr int kBwdMaxSub = SSM_BWD_MAX_SUB;
 constexpr int kBwdThreads = 256;   // main pass workgroup: 4 waves of the same stripe
 
 template <typename TA>
@@ -98,11 +101,19 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BwdArgs<TA> a) {
   const bool valid = d < a.dim;
   const int dl = valid ? d : a.dim - 1;
   float a2[NT], adj[NT];
+  const float A0 = a.A[static_cast<size_t>(dl) * NT];
+  bool pow_ok = true;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    a2[n] = a.A[static_cast<size_t>(dl) * NT + n] * kLog2e;
+    const float An = a.A[static_cast<size_t>(dl) * NT + n];
+    a2[n] = An * kLog2e;
     adj[n] = 0.0f;
+    pow_ok = pow_ok && (An == static_cast<float>(n + 1) * A0);
   }
+  // S4D-real A (every lane of the wave): e^(dt A[n]) = r^(n+1), r = e^(dt A[0]);
+  // every fourth decay is its own exponential, the three after it follow by
+  // multiplying with r (a few ulp, as in the main pass)
+  const bool pw = __all(pow_ok);
   const float bias = a.bias ? a.bias[dl] : 0.0f;
   const int s = c * a.Ls;
   const int e = (s + a.Ls < a.L) ? s + a.Ls : a.L;
@@ -116,9 +127,17 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BwdArgs<TA> a) {
     const float dy = GATE ? g * silu_f32(to_f32(a.z[i])) : g;
     float Cv[NT];
     load_row<NT, true>(a.C + (static_cast<size_t>(b) * a.L + t) * NT, NT, Cv);
+    float dA[NT];
+    if (pw) {
+      const float r = __builtin_amdgcn_exp2f(dt * a2[0]);
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      adj[n] = __builtin_fmaf(Cv[n], dy, adj[n]) * __builtin_amdgcn_exp2f(dt * a2[n]);
+      for (int n = 0; n < NT; ++n) dA[n] = (n % 4 == 0) ? __builtin_amdgcn_exp2f(dt * a2[n]) : dA[n - 1] * r;
+    } else {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) dA[n] = __builtin_amdgcn_exp2f(dt * a2[n]);
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) adj[n] = __builtin_fmaf(Cv[n], dy, adj[n]) * dA[n];
   }
   if (valid) {
     a.rS[(static_cast<size_t>(b) * (a.K - 1) + (a.K - 1 - c)) * a.dim + d] = S;
@@ -164,25 +183,46 @@ __device__ __forceinline__ float sum_group(float v) {
 // over the wave's channels (the lanes with the same state group), as a
 // reduce-scatter: each exchange across lane bit 5, 4, 3 sends half of the
 // remaining values and keeps the other half, so 8 values cost 4 + 2 + 1
-// shuffles, then full exchanges over the bits from 2 down to the group
+// exchanges, then full exchanges over the bits from 2 down to the group
 // size.  Returns the sum of value ((lane>>5)&1)*4 + ((lane>>4)&1)*2 +
 // ((lane>>3)&1) for the lane's state group; lanes differing only in bits
 // 2..log2(G) hold the same sum.
+//   bits 5 and 4: v_permlane32_swap / v_permlane16_swap (checked on the
+//     device): swapping (x, y) leaves a lane of the lower half with its own x
+//     and its partner's x, a lane of the upper half with its partner's y and
+//     its own y, so x + y is the kept half's pair sum in every lane, with no
+//     selects and no LDS;
+//   bit 3: DPP row rotate by 8 (the partner within the row of 16);
+//   bits 2..: ds_swizzle exchanges (xor within 32 lanes).
+__device__ __forceinline__ float sum_swap32(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_swap16(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+constexpr int kDppRowRor8 = 0x128;
+template <int O>
+__device__ __forceinline__ float swizzle_xor(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (O << 10) | 0x1F));
+}
 template <int G>
 __device__ __forceinline__ float reduce_scatter8(const float (&v)[8]) {
   const int lane = static_cast<int>(threadIdx.x & 63);
-  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
   float w4[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    w4[j] = (b5 ? v[j + 4] : v[j]) + __shfl_xor(b5 ? v[j] : v[j + 4], 32);
+  for (int j = 0; j < 4; ++j) w4[j] = sum_swap32(v[j], v[j + 4]);
   float w2[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    w2[j] = (b4 ? w4[j + 2] : w4[j]) + __shfl_xor(b4 ? w4[j] : w4[j + 2], 16);
-  float w = (b3 ? w2[1] : w2[0]) + __shfl_xor(b3 ? w2[0] : w2[1], 8);
-#pragma unroll
-  for (int o = 4; o >= G; o >>= 1) w += __shfl_xor(w, o);
+  for (int j = 0; j < 2; ++j) w2[j] = sum_swap16(w4[j], w4[j + 2]);
+  const bool b3 = lane & 8;
+  const float keep = b3 ? w2[1] : w2[0], send = b3 ? w2[0] : w2[1];
+  float w = keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), kDppRowRor8, 0xf,
+                                                           0xf, false));
+  if constexpr (G <= 4) w += swizzle_xor<4>(w);
+  if constexpr (G <= 2) w += swizzle_xor<2>(w);
+  if constexpr (G <= 1) w += swizzle_xor<1>(w);
   return w;
 }
 
@@ -204,7 +244,6 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
   const int64_t b = blockIdx.z;
   const bool valid = d < a.dim;
   const int dl = valid ? d : a.dim - 1;
-  const float vmask = valid ? 1.0f : 0.0f;
   const int N = NT;
   const int s = c * a.Ls;
   const int e = (s + a.Ls < a.L) ? s + a.Ls : a.L;
@@ -261,18 +300,21 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
 
   // 4a. forward over the stripe with a checkpoint every kBwdSub tokens (in
   // LDS: each lane reads back only its own)
+  // (the state after the last sub-chunk is not needed)
   const int nsub = (len + kBwdSub - 1) / kBwdSub;
   for (int k = 0; k < nsub; ++k) {
     ckpt[k][tid] = make_float4(h[0], h[1], h[2], h[3]);
-    const int t1 = (s + (k + 1) * kBwdSub < e) ? s + (k + 1) * kBwdSub : e;
-    for (int t = s + k * kBwdSub; t < t1; ++t) fwd_step(t, h);
+    if (k == nsub - 1) break;
+    for (int t = s + k * kBwdSub; t < s + (k + 1) * kBwdSub; ++t) fwd_step(t, h);
   }
 
   // 4b. adjoint flowing into the stripe's last token from later tokens
   float adj[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if (c == a.K - 1)
+    if (!valid)  // (lanes past the channels: zero adjoint and zero dy keep every sum clean)
+      adj[j] = 0.0f;
+    else if (c == a.K - 1)
       adj[j] = a.dlast ? a.dlast[(static_cast<size_t>(b) * a.dim + dl) * N + n0 + j] : 0.0f;
     else
       adj[j] = a.rH[((static_cast<size_t>(b) * a.K + (a.K - 1 - c)) * N + n0 + j) * a.dim + dl];
@@ -324,19 +366,21 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
           dy = gv * zv * sg;
           dzv = gv * y * sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f);
         }
+        if (!valid) dy = 0.0f;
+        const float dtx = dt * xv;
         float s1p = 0.0f, s2p = 0.0f, dAv[4];
         decays(dt, dAv);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          adj[j] = __builtin_fmaf(Cv[j], dy, adj[j]);
-          pc[j] = dy * hist[i][j] * vmask;
-          const float dA = dAv[j];
-          const float q = adj[j] * dA * hp[j];
+          adj[j] = __builtin_fmaf(Cv[j], dy, adj[j]);  // adjoint of h_t
+          pc[j] = dy * hist[i][j];
+          const float an = adj[j] * dAv[j];           // adjoint of h_{t-1}
+          const float q = an * hp[j];
           dAacc[j] = __builtin_fmaf(q, dt, dAacc[j]);
           s2p = __builtin_fmaf(Aj[j], q, s2p);
           s1p = __builtin_fmaf(adj[j], Bv[j], s1p);
-          pb[j] = adj[j] * dt * xv * vmask;
-          adj[j] *= dA;
+          pb[j] = adj[j] * dtx;
+          adj[j] = an;
         }
         const float s1 = sum_group<G>(s1p), s2 = sum_group<G>(s2p);
         const float ddt = __builtin_fmaf(xv, s1, s2);
@@ -411,26 +455,45 @@ __global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(const float* __restr
   dC[i] = scv;
 }
 
-// dA[d,n] = sum over (b, stripe) of pA; dD[d], dbias[d] likewise.
+// dA[d,n] = sum over (b, stripe) of pA; dD[d], dbias[d] likewise.  Block
+// of 256 = 32 elements x 8 slice groups: group j sums the slices j, j+8, ...
+// in order, and the 8 group sums are added in order (a fixed order: the
+// result does not depend on scheduling).
+constexpr int kRedElems = 32, kRedGroups = 8;
 __global__ void __launch_bounds__(256) bwd_reduce_params_kernel(
     const float* __restrict__ pA, const float* __restrict__ pD, const float* __restrict__ pbias,
     float* __restrict__ dA, float* __restrict__ dD, float* __restrict__ dbias, int dim, int N,
     int64_t slices) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  __shared__ float part[2][kRedGroups][kRedElems];
+  const int e = threadIdx.x % kRedElems, j = threadIdx.x / kRedElems;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kRedElems + e;
   const int64_t nA = static_cast<int64_t>(dim) * N;
+  float v = 0.0f, vb = 0.0f;
   if (i < nA) {
-    float v = 0.0f;
-    for (int64_t k = 0; k < slices; ++k) v += pA[k * nA + i];
-    dA[i] = v;
+    for (int64_t k = j; k < slices; k += kRedGroups) v += pA[k * nA + i];
   } else if (i < nA + dim) {
     const int64_t d = i - nA;
-    float vd = 0.0f, vb = 0.0f;
-    for (int64_t k = 0; k < slices; ++k) {
-      vd += pD[k * dim + d];
+    for (int64_t k = j; k < slices; k += kRedGroups) {
+      v += pD[k * dim + d];
       vb += pbias[k * dim + d];
     }
-    if (dD) dD[d] = vd;
-    if (dbias) dbias[d] = vb;
+  }
+  part[0][j][e] = v;
+  part[1][j][e] = vb;
+  __syncthreads();
+  if (j == 0) {
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kRedGroups; ++g) {
+      s0 += part[0][g][e];
+      s1 += part[1][g][e];
+    }
+    if (i < nA) {
+      dA[i] = s0;
+    } else if (i < nA + dim) {
+      if (dD) dD[i - nA] = s0;
+      if (dbias) dbias[i - nA] = s1;
+    }
   }
 }
 
@@ -528,9 +591,9 @@ int launch_bwd(const BwdArgs<TA>& a, const FwdArgs<TA>& f, bool sp, bool gate, f
   hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(static_cast<unsigned>((per + 255) / 256)), dim3(256),
                      0, s, a.pB, a.pC, dB, dC, per, a.tiles);
   const int64_t np = static_cast<int64_t>(a.dim) * NT + a.dim;
-  hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3(static_cast<unsigned>((np + 255) / 256)),
-                     dim3(256), 0, s, a.pA, a.pD, a.pbias, dA, dD, dbias, a.dim, NT,
-                     a.batch * a.K);
+  hipLaunchKernelGGL(bwd_reduce_params_kernel,
+                     dim3(static_cast<unsigned>((np + kRedElems - 1) / kRedElems)), dim3(256), 0,
+                     s, a.pA, a.pD, a.pbias, dA, dD, dbias, a.dim, NT, a.batch * a.K);
   return launch_status("ssm_scan_bwd");
 }
 
