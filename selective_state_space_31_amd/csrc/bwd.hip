@@ -5,7 +5,7 @@
 // The forward keeps no (b, L, D, N) states; neither does this: it recomputes
 // them, stripe by stripe (recomputation in the backward pass, as the page
 // cited in the header describes for the original kernel).  Plan, for
-// stripes of Ls <= 128 tokens:
+// stripes of Ls <= 32 tokens:
 //   1. forward summary + carry passes (the forward's own kernels) give the
 //      state entering every stripe;
 //   2. adjoint summaries: per stripe, walked from its last token to its
@@ -15,11 +15,12 @@
 //   3. the forward's carry kernel, fed the stripes in reverse order and
 //      started from dlast_state, gives the adjoint flowing into every
 //      stripe's last token from the tokens after it;
-//   4. main pass: per stripe, G = N/4 lanes per channel, 4 states per lane.
-//      The lane runs its stripe forward from the entering state, keeping a
-//      checkpoint of its 4 states every 16 tokens, then takes the 16-token
-//      sub-chunks from last to first: recompute the sub-chunk's states into
-//      registers, walk it backwards with the adjoint.  Per-token gradients
+//   4. main pass: per stripe, SPL = min(N, 8) states per lane (N/SPL lanes
+//      per channel).  The lane runs its stripe forward from the entering
+//      state, keeping a checkpoint of its states every SUB = 64/SPL tokens,
+//      then takes the sub-chunks from last to first: recompute the
+//      sub-chunk's states into registers (64 floats of history), walk it
+//      backwards with the adjoint.  Per-token gradients
 //      (dx, ddelta, dz) are stored at once; dB and dC, sums over channels,
 //      are reduced across the wave's channels by lane shuffles and across
 //      the workgroup's 4 waves in LDS into one partial per workgroup;
@@ -44,12 +45,20 @@ namespace ssm {
                                                       hipStream_t);
 SSM_BWD_STATE_INSTANCES(SSM_EXTERN_STATES)
 
-#ifndef SSM_BWD_MAX_SUB
-#define SSM_BWD_MAX_SUB 2  // sub-chunks per stripe at most
-#endif
-constexpr int kBwdSub = 16;        // tokens per recomputed sub-chunk
-constexpr int kBwdMaxSub = SSM_BWD_MAX_SUB;
+constexpr int kBwdStripe = 32;     // tokens per stripe at most (a multiple of 16)
 constexpr int kBwdThreads = 256;   // main pass workgroup: 4 waves of the same stripe
+
+// Main-pass shape for a state width: SPL states per lane, G lanes per
+// channel, sub-chunks of SUB tokens whose states are recomputed into
+// registers (SUB x SPL = 64 floats of history per lane).
+template <int NT>
+struct BwdShape {
+  static constexpr int SPL = NT >= 8 ? 8 : NT;
+  static constexpr int G = NT / SPL;
+  static constexpr int SUB = 64 / SPL;
+  static constexpr int MAXSUB = kBwdStripe / SUB;
+  static constexpr int CPB = kBwdThreads / G;
+};
 
 template <typename TA>
 struct BwdArgs {
@@ -207,38 +216,68 @@ template <int O>
 __device__ __forceinline__ float swizzle_xor(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (O << 10) | 0x1F));
 }
-template <int G>
-__device__ __forceinline__ float reduce_scatter8(const float (&v)[8]) {
+// Reduce-scatter of V values per lane (V = 8 or 16) over the lanes of the
+// same state group: exchanges across lane bits 5, 4, 3 (and 2 for V = 16)
+// each keep half of the remaining values, then full exchanges over the
+// remaining channel bits.  The lane ends with the sum of value
+// scatter_index<V>(lane).
+template <int V>
+__device__ __forceinline__ int scatter_index(int lane) {
+  int vi = ((lane >> 5) & 1) * (V / 2) + ((lane >> 4) & 1) * (V / 4) + ((lane >> 3) & 1) * (V / 8);
+  if constexpr (V == 16) vi += (lane >> 2) & 1;
+  return vi;
+}
+template <int V, int G>
+__device__ __forceinline__ float reduce_scatter(const float (&v)[V]) {
+  static_assert(V == 8 || V == 16, "8 or 16 values");
   const int lane = static_cast<int>(threadIdx.x & 63);
-  float w4[4];
+  float w32[V / 2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) w4[j] = sum_swap32(v[j], v[j + 4]);
-  float w2[2];
+  for (int j = 0; j < V / 2; ++j) w32[j] = sum_swap32(v[j], v[j + V / 2]);
+  float w16[V / 4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) w2[j] = sum_swap16(w4[j], w4[j + 2]);
+  for (int j = 0; j < V / 4; ++j) w16[j] = sum_swap16(w32[j], w32[j + V / 4]);
   const bool b3 = lane & 8;
-  const float keep = b3 ? w2[1] : w2[0], send = b3 ? w2[0] : w2[1];
-  float w = keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), kDppRowRor8, 0xf,
+  float w8[V / 8];
+#pragma unroll
+  for (int j = 0; j < V / 8; ++j) {
+    const float keep = b3 ? w16[j + V / 8] : w16[j], send = b3 ? w16[j] : w16[j + V / 8];
+    w8[j] = keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), kDppRowRor8, 0xf,
                                                            0xf, false));
-  if constexpr (G <= 4) w += swizzle_xor<4>(w);
-  if constexpr (G <= 2) w += swizzle_xor<2>(w);
-  if constexpr (G <= 1) w += swizzle_xor<1>(w);
+  }
+  float w;
+  if constexpr (V == 16) {
+    const bool b2 = lane & 4;
+    const float keep = b2 ? w8[1] : w8[0], send = b2 ? w8[0] : w8[1];
+    w = keep + swizzle_xor<4>(send);
+    if constexpr (G <= 2) w += swizzle_xor<2>(w);
+    if constexpr (G <= 1) w += swizzle_xor<1>(w);
+  } else {
+    w = w8[0];
+    if constexpr (G <= 4) w += swizzle_xor<4>(w);
+    if constexpr (G <= 2) w += swizzle_xor<2>(w);
+    if constexpr (G <= 1) w += swizzle_xor<1>(w);
+  }
   return w;
 }
 
 template <typename TA, int NT, bool SP, bool GATE>
 __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
-  constexpr int G = NT / 4;                  // lanes per channel
-  constexpr int CPB = kBwdThreads / G;       // channels per workgroup
+  using Sh = BwdShape<NT>;
+  constexpr int SPL = Sh::SPL;  // states per lane
+  constexpr int G = Sh::G;      // lanes per channel
+  constexpr int SUB = Sh::SUB;  // tokens per recomputed sub-chunk
+  constexpr int CPB = Sh::CPB;  // channels per workgroup
+  constexpr int V = 2 * SPL;    // dB and dC terms per lane and token
   constexpr int WAVES = kBwdThreads / 64;
-  __shared__ float red[WAVES][kBwdSub][2 * NT];
-  __shared__ float4 ckpt[kBwdMaxSub][kBwdThreads];  // per-lane checkpoints (4 states)
+  __shared__ float red[WAVES][SUB][2 * NT];
+  __shared__ float ckpt[Sh::MAXSUB][SPL][kBwdThreads];  // per-lane checkpoints
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g = tid % G;
-  const int n0 = 4 * g;
+  const int n0 = SPL * g;
   const int d = blockIdx.x * CPB + tid / G;
   const int c = blockIdx.y;
   const int64_t b = blockIdx.z;
@@ -249,69 +288,115 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
   const int e = (s + a.Ls < a.L) ? s + a.Ls : a.L;
   const int len = e - s;
 
-  float Aj[4], a2[4];
+  float Aj[SPL], a2[SPL];
   const float A0 = a.A[static_cast<size_t>(dl) * N];
   bool pow_ok = true;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < SPL; ++j) {
     Aj[j] = a.A[static_cast<size_t>(dl) * N + n0 + j];
     a2[j] = Aj[j] * kLog2e;
     pow_ok = pow_ok && (Aj[j] == static_cast<float>(n0 + j + 1) * A0);
   }
-  // S4D-real A (every lane of the wave): e^(dt A[n]) = r^(n+1), r = e^(dt A[0])
+  // S4D-real A (every lane of the wave): e^(dt A[n]) = r^(n+1), r = e^(dt A[0]);
+  // every fourth decay is its own exponential, the three after it follow by
+  // multiplying with r (a few ulp)
   const bool pw = __all(pow_ok);
   const float a20 = A0 * kLog2e;
-  auto decays = [&](float dt, float (&dA)[4]) {
+  auto decays = [&](float dt, float (&dA)[SPL]) {
     if (pw) {
       const float r = __builtin_amdgcn_exp2f(dt * a20);
-      dA[0] = __builtin_amdgcn_exp2f(dt * a2[0]);
 #pragma unroll
-      for (int j = 1; j < 4; ++j) dA[j] = dA[j - 1] * r;
+      for (int j = 0; j < SPL; ++j)
+        dA[j] = (j % 4 == 0) ? __builtin_amdgcn_exp2f(dt * a2[j]) : dA[j > 0 ? j - 1 : 0] * r;
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dA[j] = __builtin_amdgcn_exp2f(dt * a2[j]);
+      for (int j = 0; j < SPL; ++j) dA[j] = __builtin_amdgcn_exp2f(dt * a2[j]);
     }
   };
   const float bias = a.bias ? a.bias[dl] : 0.0f;
   const float dsk = a.Dsk ? a.Dsk[dl] : 0.0f;
 
   // state entering the stripe
-  float h[4];
+  float h[SPL];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < SPL; ++j) {
     if (c == 0)
       h[j] = a.h0 ? a.h0[(static_cast<size_t>(b) * a.dim + dl) * N + n0 + j] : 0.0f;
     else
       h[j] = a.fH[((static_cast<size_t>(b) * a.K + c) * N + n0 + j) * a.dim + dl];
   }
 
-  // one forward token: h <- e^(dt A) h + dt B x
-  auto fwd_step = [&](int t, float (&hh)[4]) {
-    const size_t i = (static_cast<size_t>(b) * a.L + t) * a.dim + dl;
-    const float u = to_f32(a.delta[i]) + bias;
-    const float dt = SP ? softplus_f32(u) : u;
-    const float dx = dt * to_f32(a.x[i]);
-    float Bv[4], dA[4];
-    load4(a.B + (static_cast<size_t>(b) * a.L + t) * N + n0, Bv);
-    decays(dt, dA);
+  // Token rows of a sub-chunk through buffer descriptors based at its first
+  // token: the lane's column is a constant offset, the token a scalar one,
+  // and rows past the sub-chunk fall outside the range (loads read zero).
+  using IO = Io<TA>;
+  constexpr uint32_t es = sizeof(TA);
+  const uint32_t rowA = static_cast<uint32_t>(a.dim) * es;  // bytes per activation row
+  const uint32_t rowN = static_cast<uint32_t>(N) * es;      // bytes per B / C row
+  const uint32_t vo_a = static_cast<uint32_t>(dl) * es, vo_n = static_cast<uint32_t>(n0) * es;
+  struct Rows {
+    rsrc_t x, delta, B;
+  };
+  auto rows_at = [&](int t0, int t1) {
+    const size_t ra = (static_cast<size_t>(b) * a.L + t0) * a.dim;
+    const size_t rn = (static_cast<size_t>(b) * a.L + t0) * N;
+    const uint32_t n = static_cast<uint32_t>(t1 - t0);
+    return Rows{make_rsrc(a.x + ra, n * rowA), make_rsrc(a.delta + ra, n * rowA),
+                make_rsrc(a.B + rn, n * rowN)};
+  };
+  // the lane's SPL consecutive values of a B / C row
+  auto loadS = [&](rsrc_t r, uint32_t soff, float (&v)[SPL]) {
+    if constexpr (sizeof(TA) == 2) {  // 8-byte loads: B and C rows are 8-byte aligned
 #pragma unroll
-    for (int j = 0; j < 4; ++j) hh[j] = __builtin_fmaf(dA[j], hh[j], dx * Bv[j]);
+      for (int q = 0; q < SPL / 4; ++q) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, vo_n + 8 * q, soff, 0);
+        v[4 * q] = __uint_as_float(w[0] << 16);
+        v[4 * q + 1] = __uint_as_float(w[0] & 0xffff0000u);
+        v[4 * q + 2] = __uint_as_float(w[1] << 16);
+        v[4 * q + 3] = __uint_as_float(w[1] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < SPL / 4; ++q) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b128(r, vo_n + 16 * q, soff, 0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[4 * q + k] = __uint_as_float(w[k]);
+      }
+    }
   };
 
-  // 4a. forward over the stripe with a checkpoint every kBwdSub tokens (in
-  // LDS: each lane reads back only its own)
-  // (the state after the last sub-chunk is not needed)
-  const int nsub = (len + kBwdSub - 1) / kBwdSub;
+  // one forward token (row i of the sub-chunk): h <- e^(dt A) h + dt B x; returns dt
+  auto fwd_step = [&](const Rows& r, int i, float (&hh)[SPL]) {
+    const uint32_t so = static_cast<uint32_t>(i) * rowA;
+    const float u = IO::f32(IO::load(r.delta, vo_a, so)) + bias;
+    const float dt = SP ? softplus_f32(u) : u;
+    const float dx = dt * IO::f32(IO::load(r.x, vo_a, so));
+    float Bv[SPL], dA[SPL];
+    loadS(r.B, static_cast<uint32_t>(i) * rowN, Bv);
+    decays(dt, dA);
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) hh[j] = __builtin_fmaf(dA[j], hh[j], dx * Bv[j]);
+    return dt;
+  };
+
+  // 4a. forward over the stripe with a checkpoint every SUB tokens (in LDS:
+  // each lane reads back only its own); the state after the last sub-chunk
+  // is not needed
+  const int nsub = (len + SUB - 1) / SUB;
   for (int k = 0; k < nsub; ++k) {
-    ckpt[k][tid] = make_float4(h[0], h[1], h[2], h[3]);
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) ckpt[k][j][tid] = h[j];
     if (k == nsub - 1) break;
-    for (int t = s + k * kBwdSub; t < s + (k + 1) * kBwdSub; ++t) fwd_step(t, h);
+    const int t0 = s + k * SUB;
+    const Rows r = rows_at(t0, t0 + SUB);
+#pragma unroll 2
+    for (int i = 0; i < SUB; ++i) fwd_step(r, i, h);
   }
 
   // 4b. adjoint flowing into the stripe's last token from later tokens
-  float adj[4];
+  float adj[SPL];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < SPL; ++j) {
     if (!valid)  // (lanes past the channels: zero adjoint and zero dy keep every sum clean)
       adj[j] = 0.0f;
     else if (c == a.K - 1)
@@ -319,103 +404,118 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
     else
       adj[j] = a.rH[((static_cast<size_t>(b) * a.K + (a.K - 1 - c)) * N + n0 + j) * a.dim + dl];
   }
-  float dAacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float dAacc[SPL];
+#pragma unroll
+  for (int j = 0; j < SPL; ++j) dAacc[j] = 0.0f;
   float dDacc = 0.0f, dbacc = 0.0f;
 
   // 4c. sub-chunks from last to first (nsub is uniform over the workgroup)
   for (int k = nsub - 1; k >= 0; --k) {
-    const int t0 = s + k * kBwdSub;
-    float ck[4], hist[kBwdSub][4];
+    const int t0 = s + k * SUB;
+    const int t1 = (t0 + SUB < e) ? t0 + SUB : e;
+    const Rows r = rows_at(t0, t1);
+    const size_t ra = (static_cast<size_t>(b) * a.L + t0) * a.dim;
+    const uint32_t nbytes = static_cast<uint32_t>(t1 - t0) * rowA;
+    const rsrc_t rdo = make_rsrc(a.dout + ra, nbytes);
+    const rsrc_t rz = make_rsrc(GATE ? a.z + ra : a.x + ra, nbytes);
+    const rsrc_t rC = make_rsrc(a.C + (static_cast<size_t>(b) * a.L + t0) * N,
+                                static_cast<uint32_t>(t1 - t0) * rowN);
+    // gradients of the per-token rows: only lane 0 of each channel stores
+    // (the others store past every descriptor's range, which the hardware
+    // drops; byte ranges here stay below 2^30)
+    const rsrc_t rdx = make_rsrc(a.dx + ra, nbytes), rdd = make_rsrc(a.ddelta + ra, nbytes);
+    const rsrc_t rdz = make_rsrc(GATE ? a.dz + ra : a.dx + ra, GATE ? nbytes : 0);
+    const uint32_t vo_st = (g == 0 && valid) ? vo_a : kOutOfRange;
+    float ck[SPL], hist[SUB][SPL], dts[SUB];
     {
-      const float4 v = ckpt[k][tid];
-      ck[0] = v.x; ck[1] = v.y; ck[2] = v.z; ck[3] = v.w;
-      float hc[4] = {ck[0], ck[1], ck[2], ck[3]};
 #pragma unroll
-      for (int i = 0; i < kBwdSub; ++i) {
-        if (t0 + i < e) fwd_step(t0 + i, hc);
+      for (int j = 0; j < SPL; ++j) ck[j] = ckpt[k][j][tid];
+      float hc[SPL];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) hist[i][j] = hc[j];
+      for (int j = 0; j < SPL; ++j) hc[j] = ck[j];
+#pragma unroll
+      for (int i = 0; i < SUB; ++i) {
+        dts[i] = 0.0f;
+        if (t0 + i < e) dts[i] = fwd_step(r, i, hc);
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) hist[i][j] = hc[j];
       }
     }
 #pragma unroll
-    for (int i = kBwdSub - 1; i >= 0; --i) {
+    for (int i = SUB - 1; i >= 0; --i) {
       const int t = t0 + i;
-      float pb[4] = {0.0f, 0.0f, 0.0f, 0.0f}, pc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (t < e) {
-        const size_t ix = (static_cast<size_t>(b) * a.L + t) * a.dim + dl;
-        const size_t row = (static_cast<size_t>(b) * a.L + t) * N + n0;
-        const float u = to_f32(a.delta[ix]) + bias;
-        const float dt = SP ? softplus_f32(u) : u;
-        const float xv = to_f32(a.x[ix]);
-        float Bv[4], Cv[4];
-        load4(a.B + row, Bv);
-        load4(a.C + row, Cv);
-        float hp[4];
+      float pv[V];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) hp[j] = (i > 0) ? hist[i > 0 ? i - 1 : 0][j] : ck[j];
-        // readout of this token (all 16 states: sum over the channel's lanes)
+      for (int j = 0; j < V; ++j) pv[j] = 0.0f;
+      if (t < e) {
+        const uint32_t so = static_cast<uint32_t>(i) * rowA, son = static_cast<uint32_t>(i) * rowN;
+        const float u = IO::f32(IO::load(r.delta, vo_a, so)) + bias;
+        const float dt = dts[i];
+        const float xv = IO::f32(IO::load(r.x, vo_a, so));
+        float Bv[SPL], Cv[SPL];
+        loadS(r.B, son, Bv);
+        loadS(rC, son, Cv);
+        // readout of this token (all states: sum over the channel's lanes)
         float yp = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) yp = __builtin_fmaf(Cv[j], hist[i][j], yp);
+        for (int j = 0; j < SPL; ++j) yp = __builtin_fmaf(Cv[j], hist[i][j], yp);
         const float y = sum_group<G>(yp) + dsk * xv;
-        const float gv = to_f32(a.dout[ix]);
+        const float gv = IO::f32(IO::load(rdo, vo_a, so));
         float dy = gv, dzv = 0.0f;
         if constexpr (GATE) {
-          const float zv = to_f32(a.z[ix]);
+          const float zv = IO::f32(IO::load(rz, vo_a, so));
           const float sg = sigmoid_f32(zv);
           dy = gv * zv * sg;
           dzv = gv * y * sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f);
         }
         if (!valid) dy = 0.0f;
         const float dtx = dt * xv;
-        float s1p = 0.0f, s2p = 0.0f, dAv[4];
+        float s1p = 0.0f, s2p = 0.0f, dAv[SPL];
         decays(dt, dAv);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < SPL; ++j) {
+          const float hp = (i > 0) ? hist[i > 0 ? i - 1 : 0][j] : ck[j];
           adj[j] = __builtin_fmaf(Cv[j], dy, adj[j]);  // adjoint of h_t
-          pc[j] = dy * hist[i][j];
+          pv[SPL + j] = dy * hist[i][j];              // dC term
           const float an = adj[j] * dAv[j];           // adjoint of h_{t-1}
-          const float q = an * hp[j];
+          const float q = an * hp;
           dAacc[j] = __builtin_fmaf(q, dt, dAacc[j]);
           s2p = __builtin_fmaf(Aj[j], q, s2p);
           s1p = __builtin_fmaf(adj[j], Bv[j], s1p);
-          pb[j] = adj[j] * dtx;
+          pv[j] = adj[j] * dtx;                       // dB term
           adj[j] = an;
         }
         const float s1 = sum_group<G>(s1p), s2 = sum_group<G>(s2p);
         const float ddt = __builtin_fmaf(xv, s1, s2);
         const float dxv = __builtin_fmaf(dt, s1, dsk * dy);
         const float dd = SP ? ddt * sigmoid_f32(u) : ddt;
-        if (g == 0 && valid) {
-          store_act(a.dx + ix, dxv);
-          store_act(a.ddelta + ix, dd);
-          if constexpr (GATE) store_act(a.dz + ix, dzv);
-        }
+        IO::store(dxv, rdx, vo_st, so);
+        IO::store(dd, rdd, vo_st, so);
+        if constexpr (GATE) IO::store(dzv, rdz, vo_st, so);
         dDacc = __builtin_fmaf(dy, xv, dDacc);
         dbacc += dd;
       }
       // dB, dC of this token: sum over the wave's channels
       {
-        const float v8[8] = {pb[0], pb[1], pb[2], pb[3], pc[0], pc[1], pc[2], pc[3]};
-        const float w = reduce_scatter8<G>(v8);
-        if ((lane & (8 - G)) == 0) {
-          const int vi = ((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
-          red[wave][i][(vi < 4 ? 0 : NT) + n0 + (vi & 3)] = w;
+        const float w = reduce_scatter<V, G>(pv);
+        if ((lane & (64 / V - 1) & ~(G - 1)) == 0) {
+          const int vi = scatter_index<V>(lane);
+          red[wave][i][(vi < SPL ? 0 : NT) + n0 + (vi % SPL)] = w;
         }
       }
     }
     // sum over the workgroup's waves; one partial per (tile, b, t, n)
     __syncthreads();
-    for (int idx = tid; idx < kBwdSub * 2 * NT; idx += kBwdThreads) {
+    for (int idx = tid; idx < SUB * 2 * NT; idx += kBwdThreads) {
       const int i = idx / (2 * NT);
-      const int r = idx % (2 * NT);
+      const int rr = idx % (2 * NT);
       const int t = t0 + i;
       if (t < e) {
         float v = 0.0f;
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) v += red[w][i][r];
-        float* dst = r < NT ? a.pB : a.pC;
-        dst[((static_cast<size_t>(blockIdx.x) * a.batch + b) * a.L + t) * N + (r % NT)] = v;
+        for (int w = 0; w < WAVES; ++w) v += red[w][i][rr];
+        float* dst = rr < NT ? a.pB : a.pC;
+        dst[((static_cast<size_t>(blockIdx.x) * a.batch + b) * a.L + t) * N + (rr % NT)] = v;
       }
     }
     __syncthreads();
@@ -424,14 +524,15 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
   if (valid) {
     const size_t sc = static_cast<size_t>(b) * a.K + c;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a.pA[(sc * a.dim + d) * N + n0 + j] = dAacc[j];
+    for (int j = 0; j < SPL; ++j) a.pA[(sc * a.dim + d) * N + n0 + j] = dAacc[j];
     if (g == 0) {
       a.pD[sc * a.dim + d] = dDacc;
       a.pbias[sc * a.dim + d] = dbacc;
     }
     if (c == 0 && a.dh0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a.dh0[(static_cast<size_t>(b) * a.dim + d) * N + n0 + j] = adj[j];
+      for (int j = 0; j < SPL; ++j)
+        a.dh0[(static_cast<size_t>(b) * a.dim + d) * N + n0 + j] = adj[j];
     }
   }
 }
@@ -520,17 +621,18 @@ struct BwdPlan {
 
 BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N) {
   BwdPlan p;
-  const int G = static_cast<int>(N / 4);
-  const int cpb = kBwdThreads / G;
+  const int cpb = N == 16 ? BwdShape<16>::CPB : N == 8 ? BwdShape<8>::CPB : BwdShape<4>::CPB;
   p.tiles = static_cast<int>((dim + cpb - 1) / cpb);
-  // enough workgroups for about 3 waves per SIMD, stripes of whole sub-chunks
+  // enough workgroups for about 3 waves per SIMD; stripes are a multiple of
+  // 16 tokens (whole sub-chunks, and whole token pairs-of-groups for the
+  // forward summary pass that gives their entering states), at most kBwdStripe
   const int64_t per_stripe = static_cast<int64_t>(p.tiles) * batch * (kBwdThreads / 64);
   const int64_t target = 3LL * 4 * device_cus();
   int64_t K = (target + per_stripe - 1) / per_stripe;
   if (K < 1) K = 1;
-  int64_t Ls = L > 0 ? (L + K - 1) / K : kBwdSub;
-  Ls = (Ls + kBwdSub - 1) / kBwdSub * kBwdSub;
-  if (Ls > kBwdSub * kBwdMaxSub) Ls = kBwdSub * kBwdMaxSub;
+  int64_t Ls = L > 0 ? (L + K - 1) / K : 16;
+  Ls = (Ls + 15) / 16 * 16;
+  if (Ls > kBwdStripe) Ls = kBwdStripe;
   K = L > 0 ? (L + Ls - 1) / Ls : 1;
   p.Ls = static_cast<int>(Ls);
   p.K = static_cast<int>(K);
