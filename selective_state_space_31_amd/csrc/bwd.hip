@@ -119,34 +119,48 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BwdArgs<TA> a) {
     adj[n] = 0.0f;
     pow_ok = pow_ok && (An == static_cast<float>(n + 1) * A0);
   }
-  // S4D-real A (every lane of the wave): e^(dt A[n]) = r^(n+1), r = e^(dt A[0]);
-  // every fourth decay is its own exponential, the three after it follow by
-  // multiplying with r (a few ulp, as in the main pass)
   const bool pw = __all(pow_ok);
   const float bias = a.bias ? a.bias[dl] : 0.0f;
   const int s = c * a.Ls;
   const int e = (s + a.Ls < a.L) ? s + a.Ls : a.L;
   float S = 0.0f;
-  for (int t = e - 1; t >= s; --t) {
+  auto token = [&](int t, float& dt, float& dy, float (&Cv)[NT]) {
     const size_t i = (static_cast<size_t>(b) * a.L + t) * a.dim + dl;
     const float u = to_f32(a.delta[i]) + bias;
-    const float dt = SP ? softplus_f32(u) : u;
-    S += dt;
+    dt = SP ? softplus_f32(u) : u;
     const float g = to_f32(a.dout[i]);
-    const float dy = GATE ? g * silu_f32(to_f32(a.z[i])) : g;
-    float Cv[NT];
+    dy = GATE ? g * silu_f32(to_f32(a.z[i])) : g;
     load_row<NT, true>(a.C + (static_cast<size_t>(b) * a.L + t) * NT, NT, Cv);
-    float dA[NT];
-    if (pw) {
-      const float r = __builtin_amdgcn_exp2f(dt * a2[0]);
+  };
+  // The summary is sum_t (prod_{u=s..t} e^(dt_u A)) C_t dy_t.  S4D-real A
+  // (every lane of the wave): e^(dt A[n]) = r^(n+1), r = e^(dt A[0]), so walking
+  // the stripe forward with P = prod_{u<=t} r_u the weight of state n is
+  // dy_t P^(n+1), a chain of multiplies: one multiply and one FMA per state
+  // (the mirror of the forward summary pass).  Otherwise the walk runs
+  // backwards, a <- (a + C_t dy_t) e^(dt_t A), one exponential per state.
+  if (pw) {
+    float P = 1.0f;
+    for (int t = s; t < e; ++t) {
+      float dt, dy, Cv[NT];
+      token(t, dt, dy, Cv);
+      S += dt;
+      P *= __builtin_amdgcn_exp2f(dt * a2[0]);
+      float wgt = dy * P;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) dA[n] = (n % 4 == 0) ? __builtin_amdgcn_exp2f(dt * a2[n]) : dA[n - 1] * r;
-    } else {
-#pragma unroll
-      for (int n = 0; n < NT; ++n) dA[n] = __builtin_amdgcn_exp2f(dt * a2[n]);
+      for (int n = 0; n < NT; ++n) {
+        adj[n] = __builtin_fmaf(wgt, Cv[n], adj[n]);
+        wgt *= P;
+      }
     }
+  } else {
+    for (int t = e - 1; t >= s; --t) {
+      float dt, dy, Cv[NT];
+      token(t, dt, dy, Cv);
+      S += dt;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) adj[n] = __builtin_fmaf(Cv[n], dy, adj[n]) * dA[n];
+      for (int n = 0; n < NT; ++n)
+        adj[n] = __builtin_fmaf(Cv[n], dy, adj[n]) * __builtin_amdgcn_exp2f(dt * a2[n]);
+    }
   }
   if (valid) {
     a.rS[(static_cast<size_t>(b) * (a.K - 1) + (a.K - 1 - c)) * a.dim + d] = S;
