@@ -173,20 +173,6 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BwdArgs<TA> a) {
 // ----------------------------------------------------------------------------
 // 4. main pass
 // ----------------------------------------------------------------------------
-// Four consecutive values of a (b, L, N) row: one 16-byte (float32) or
-// 8-byte (bf16) load per lane.
-__device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
-  const float4 q = *reinterpret_cast<const float4*>(p);
-  v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-}
-__device__ __forceinline__ void load4(const bf16_t* p, float (&v)[4]) {
-  const uint2 q = *reinterpret_cast<const uint2*>(p);
-  v[0] = __uint_as_float(q.x << 16);
-  v[1] = __uint_as_float(q.x & 0xffff0000u);
-  v[2] = __uint_as_float(q.y << 16);
-  v[3] = __uint_as_float(q.y & 0xffff0000u);
-}
-
 // Sum over the G lanes of one channel (adjacent lanes of a quad): DPP quad
 // permutations, no LDS traffic.
 constexpr int kDppQuadXor1 = 0xB1;  // quad_perm(1,0,3,2)

@@ -31,7 +31,10 @@
 // scalar offsets, and rows past the sequence end fall outside the
 // descriptor's range (loads read zero, stores are dropped).  The next
 // chunk's inputs are fetched into registers while the current one is
-// computed.
+// computed.  A wave's outputs cover only 32 bytes of each token row, so they
+// are staged (float32, before the gate) in the LDS that C and S used, and
+// every wave then gates and stores 16 whole 128-byte rows: a quarter of the
+// memory requests that storing the accumulator layout directly would make.
 //
 // When (b, h) pairs alone do not fill the chip, the sequence is cut into
 // segments: a state pass runs every segment but the last from a zero state
@@ -98,8 +101,6 @@ struct SsdArgs {
   int cps;  // chunks per segment
   int nseg;
 };
-
-__device__ __forceinline__ float exp_f(float v) { return __builtin_amdgcn_exp2f(v * kLog2e); }
 
 // v shifted across lanes by a DPP pattern; lanes without a source read 0
 template <int CTRL, int ROWS>
