@@ -37,10 +37,11 @@
 // memory requests that storing the accumulator layout directly would make.
 //
 // When (b, h) pairs alone do not fill the chip, the sequence is cut into
-// segments: a state pass runs every segment but the last from a zero state
-// (state update only) and leaves its end state and total log-decay; the
-// output pass of segment s starts from the state entering it, composed from
-// the initial state and the end states of segments 0..s-1.
+// segments: a state pass runs every segment but the last (state update
+// only; segment 0 from the initial state, the others from zero) and leaves
+// its end state and total log-decay; the output pass of segment s starts
+// from the state entering it, composed from the end states of segments
+// 0..s-1 (segment 0 from a copy of the initial state the state pass left).
 //
 // MFMA operand layout (16x16x32 bf16; checked on the device): lane l holds
 // A[l%16][8*(l/16) + i] and B[8*(l/16) + i][l%16], i = 0..7; accumulator
@@ -92,7 +93,10 @@ struct SsdArgs {
   float* last_state;
   const float* h0;
   float* seg_state;  // (batch, nseg-1, H) blocks of P*N floats: end state of segment s
-                     // run from zero, in the waves' accumulator order
+                     // (segment 0 from the initial state, the others from zero), in
+                     // the waves' accumulator order
+  float* h0_copy;    // (batch, H) blocks of P*N floats: the initial state in the same
+                     // order, for the output pass of segment 0
   float* seg_lam;    // (batch, nseg-1, H): sum of dt A over segment s
   int L;
   int H;
@@ -261,16 +265,34 @@ ssd_fwd_kernel(SsdArgs a) {
   const int64_t bh = b * H + h;
 
   // ---- the state entering the segment ----
+  // With one segment, its workgroup reads the initial state and writes the
+  // final state itself (in place is safe).  With several, the initial state
+  // is read only by the state pass (segment 0 starts from it and leaves a
+  // copy for the output pass), which finishes before the output pass writes
+  // the final state: the output pass never reads the caller's initial_state,
+  // which may be the last_state buffer.
   f32x4 st[NT];
 #pragma unroll
   for (int nb = 0; nb < NT; ++nb) st[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool h0_direct = a.h0 && (FULL ? a.nseg == 1 : seg == 0);
+  if (h0_direct) {
+    const float* src = a.h0 + (bh * P + 16 * w + m) * NS;
+#pragma unroll
+    for (int nb = 0; nb < NT; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[nb][r] = src[nmap(nb, q) + r];
+    if (!FULL) {
+      f32x4* cp = reinterpret_cast<f32x4*>(a.h0_copy + static_cast<size_t>(bh) * P * NS) + w * NT * 64;
+#pragma unroll
+      for (int nb = 0; nb < NT; ++nb) cp[nb * 64 + lane] = st[nb];
+    }
+  }
   if constexpr (FULL) {
-    if (a.h0) {
-      const float* src = a.h0 + (bh * P + 16 * w + m) * NS;
+    if (a.h0 && a.nseg > 1 && seg == 0) {
+      const f32x4* cp =
+          reinterpret_cast<const f32x4*>(a.h0_copy + static_cast<size_t>(bh) * P * NS) + w * NT * 64;
 #pragma unroll
-      for (int nb = 0; nb < NT; ++nb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st[nb][r] = src[nmap(nb, q) + r];
+      for (int nb = 0; nb < NT; ++nb) st[nb] = cp[nb * 64 + lane];
     }
     for (int j = 0; j < seg; ++j) {
       const size_t slot = (static_cast<size_t>(b) * (a.nseg - 1) + j) * H + h;
@@ -586,9 +608,12 @@ SsdPlan plan_ssd(int64_t batch, int64_t L, int64_t H) {
   return SsdPlan{static_cast<int>(cps), static_cast<int>(nseg)};
 }
 
+// Workspace (only with several segments): the segments' end states
+// (nseg - 1 per (sequence, head)), a copy of the initial state per
+// (sequence, head), then the segments' log-decays.
 size_t ssd_workspace(int64_t batch, int64_t H, int64_t P, int64_t N, const SsdPlan& p) {
   if (p.nseg <= 1) return 0;
-  const size_t states = static_cast<size_t>(batch) * (p.nseg - 1) * H * P * N * 4;
+  const size_t states = static_cast<size_t>(batch) * p.nseg * H * P * N * 4;
   return (states + 255) / 256 * 256 + static_cast<size_t>(batch) * (p.nseg - 1) * H * 4;
 }
 
@@ -665,15 +690,17 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* dt_bias, int dt_soft
   for (const auto& o : outs)
     if (overlap(wsp, o)) return fail(SSM_ERR_ALIAS, "%s: workspace overlaps output %s", fn, o.name);
   if (seqlen == 0 && !last_state) return SSM_OK;
-  const size_t sbytes = static_cast<size_t>(batch) * (plan.nseg - 1) * nheads * headdim * dstate * 4;
+  const size_t slot_floats = static_cast<size_t>(batch) * nheads * headdim * dstate;
+  const size_t sbytes = slot_floats * plan.nseg * 4;
   float* seg_state = need ? static_cast<float*>(workspace) : nullptr;
+  float* h0_copy = need ? seg_state + slot_floats * (plan.nseg - 1) : nullptr;
   float* seg_lam = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                    (sbytes + 255) / 256 * 256)
                         : nullptr;
   SsdArgs args{static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(dt), dt_bias, A,
                static_cast<const bf16_t*>(B), static_cast<const bf16_t*>(C), D,
                static_cast<const bf16_t*>(z), static_cast<bf16_t*>(out), last_state,
-               initial_state, seg_state, seg_lam, static_cast<int>(seqlen),
+               initial_state, seg_state, h0_copy, seg_lam, static_cast<int>(seqlen),
                static_cast<int>(nheads), static_cast<int>(ngroups), dt_softplus, plan.cps,
                plan.nseg};
   const dim3 block(kSsdThreads);

@@ -107,6 +107,22 @@ def test_resume_in_place_and_split():
     close(host(st), ref_last, "split last_state")
 
 
+def test_resume_in_place_over_segments():
+    """Many segments (batch 1, 4 heads, 1000 tokens) with last_state written
+    over initial_state: the output pass must not read the caller's initial
+    state after the last segment has overwritten it."""
+    p = make_ssd_problem(1, 1000, 4, 64, 128, 1, seed=23, device=DEV, initial_state=True)
+    h0 = p.h0.clone()
+    st = p.h0.clone()
+    out, _ = ssm_ssd_fwd(p.x, p.dt, p.A, p.B, p.C, D=p.D, z=p.z, dt_bias=p.dt_bias,
+                         initial_state=st, last_state=st)
+    torch.cuda.synchronize()
+    ref, ref_last = oracle.ssd_scan(host(p.x), host(p.dt), host(p.A), host(p.B), host(p.C),
+                                    D=host(p.D), z=host(p.z), dt_bias=host(p.dt_bias), h0=host(h0))
+    close(host(out), ref, "in place out")
+    close(host(st), ref_last, "in place last_state")
+
+
 def test_config_ssd_mamba2_2p7b_bf16_sampled_heads():
     c = SSD_CONFIGS["ssd_mamba2_2p7b_bf16"]
     p = make_ssd_problem(**c, seed=0, device=DEV, engine="torch_cuda")
