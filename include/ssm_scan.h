@@ -238,7 +238,8 @@ size_t ssm_ssd_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads
  *   B, C        : (batch, dstate) act
  *   delta_bias, D_skip : (dim) float32 or NULL;  A : (dim, dstate) float32
  * Equivalent to ssm_scan_fwd with seqlen = 1 and initial_state = last_state =
- * state.
+ * state.  One launch: batch * dim * (dstate / 4 when dstate % 4 == 0, else 1)
+ * must stay below 2^31 - 256 (SSM_ERR_SHAPE otherwise).
  */
 int ssm_state_update(float* state, const void* x, const void* delta, const float* delta_bias,
                      int delta_softplus, const float* A, const void* B, const void* C,

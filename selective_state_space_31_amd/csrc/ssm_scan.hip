@@ -239,160 +239,97 @@ struct DecArgs {
   int softplus;
 };
 
-// G lanes per channel, 4 consecutive states per lane (N = 4G): each wave
-// reads and writes one contiguous 1 KiB stretch of the state per instruction.
-template <typename TA, int G>
-__global__ void __launch_bounds__(256) decode_vec_kernel(DecArgs<TA> a) {
-  constexpr int N = 4 * G;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t nch = a.batch * a.dim;
-  const int64_t ch = gid / G;
-  const int q = static_cast<int>(gid % G);
-  const bool valid = ch < nch;
-  const int64_t c = valid ? ch : nch - 1;
-  const int64_t b = c / a.dim;
-  const int d = static_cast<int>(c % a.dim);
+// Four consecutive values of a B or C row (the row start is aligned to 4
+// elements, so float32 rows give one 16-byte load, bf16 rows one 8-byte load).
+__device__ __forceinline__ void load_quad(const float* p, float (&v)[4]) {
+  const float4 w = *reinterpret_cast<const float4*>(p);
+  v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+}
+__device__ __forceinline__ void load_quad(const bf16_t* p, float (&v)[4]) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(w.x << 16);
+  v[1] = __uint_as_float(w.x & 0xffff0000u);
+  v[2] = __uint_as_float(w.y << 16);
+  v[3] = __uint_as_float(w.y & 0xffff0000u);
+}
 
-  float4* sp = reinterpret_cast<float4*>(a.state + c * N) + q;
-  const float4 hv = *sp;
-  const float4 Av = reinterpret_cast<const float4*>(a.A + static_cast<size_t>(d) * N)[q];
-  float Bv[4], Cv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    Bv[i] = to_f32(a.B[b * N + 4 * q + i]);
-    Cv[i] = to_f32(a.C[b * N + 4 * q + i]);
-  }
+// The state is touched once per step, so its 16-byte accesses carry the
+// nontemporal hint: streamed through the caches instead of kept in them
+// (measured on the 256 x 5120 x 16 step: 44.5 -> 36 us).
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4_t load_stream(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+}
+__device__ __forceinline__ void store_stream(float* p, f32x4_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
+}
+
+// dstate = 4G (G = 1, 2, 4, 8, 16): G lanes per (sequence, channel), each
+// owning 4 consecutive states, so a wave's state accesses are one contiguous
+// 1 KiB stretch per instruction.  The lanes of a channel each compute the
+// channel's softplus (cheaper than sharing it: the step is bound by HBM) and
+// sum their partial readouts with G-lane shuffles.  When every channel of the
+// wave has A of the S4D-real shape, A[n] = (n+1) A[0], the lane's decays are
+// e^(Delta A[4q]) and three further factors r = e^(Delta A[0]) applied against
+// r's two-float value; otherwise every decay is its own accurate exponential.
+template <typename TA, int G>
+__global__ void __launch_bounds__(256) decode_quad_kernel(DecArgs<TA> a) {
+  constexpr int N = 4 * G;
+  // lane counts stay below 2^31 (checked on the host): 32-bit index arithmetic
+  const uint32_t nch = static_cast<uint32_t>(a.batch * a.dim);
+  const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+  const bool valid = gid < nch * G;
+  const uint32_t c = valid ? gid / G : nch - 1;
+  const int q = static_cast<int>(gid % G);
+  float* sp = a.state + static_cast<size_t>(c) * N + 4 * q;
+  const f32x4_t hv = load_stream(sp);
   const float xv = to_f32(a.x[c]);
-  const float raw = to_f32(a.delta[c]) + (a.bias ? a.bias[d] : 0.0f);
+  const float raw0 = to_f32(a.delta[c]);
+  const float zv = a.z ? to_f32(a.z[c]) : 0.0f;
+  const uint32_t b = c / static_cast<uint32_t>(a.dim);
+  const int d = static_cast<int>(c - b * static_cast<uint32_t>(a.dim));
+  const float4 Av = *reinterpret_cast<const float4*>(a.A + static_cast<size_t>(d) * N + 4 * q);
+  const float A0 = a.A[static_cast<size_t>(d) * N];
+  float Bv[4], Cv[4];
+  load_quad(a.B + static_cast<size_t>(b) * N + 4 * q, Bv);
+  load_quad(a.C + static_cast<size_t>(b) * N + 4 * q, Cv);
+  const float raw = raw0 + (a.bias ? a.bias[d] : 0.0f);
   const float dt = a.softplus ? softplus_f32(raw) : raw;
   const float dx = dt * xv;
-  float h[4] = {hv.x, hv.y, hv.z, hv.w};
+  float h[4] = {hv[0], hv[1], hv[2], hv[3]};
   const float Aa[4] = {Av.x, Av.y, Av.z, Av.w};
-  float y = 0.0f;
+  bool pow_ok = true;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float unused;
-    const float dA = exp_acc(dt * Aa[i], unused);  // HBM-bound: the accurate exp is free here
-    h[i] = __builtin_fmaf(dA, h[i], dx * Bv[i]);
-    y = __builtin_fmaf(Cv[i], h[i], y);
+  for (int i = 0; i < 4; ++i) pow_ok = pow_ok && (Aa[i] == static_cast<float>(4 * q + i + 1) * A0);
+  float y = 0.0f;
+  if (__all(pow_ok)) {
+    float rl, pl;
+    const float rh = exp_acc(dt * A0, rl);
+    float p = exp_acc(dt * Aa[0], pl);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = __builtin_fmaf(p, h[i], dx * Bv[i]);
+      y = __builtin_fmaf(Cv[i], h[i], y);
+      if (i < 3) p = __builtin_fmaf(p, rh, p * rl);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float unused;
+      h[i] = __builtin_fmaf(exp_acc(dt * Aa[i], unused), h[i], dx * Bv[i]);
+      y = __builtin_fmaf(Cv[i], h[i], y);
+    }
   }
   // sum the partial readouts of the G lanes of this channel
 #pragma unroll
   for (int s = 1; s < G; s <<= 1) y += __shfl_xor(y, s, G);
   if (valid) {
-    *sp = make_float4(h[0], h[1], h[2], h[3]);
+    store_stream(sp, f32x4_t{h[0], h[1], h[2], h[3]});
     if (q == 0) {
       y += (a.Dsk ? a.Dsk[d] : 0.0f) * xv;
-      if (a.z) y *= silu_f32(to_f32(a.z[c]));
+      if (a.z) y *= silu_f32(zv);
       store_act(a.out + c, y);
     }
-  }
-}
-
-// NT values of a B or C row as 16-byte vector loads (row start 16-byte aligned).
-template <int NT>
-__device__ __forceinline__ void load_row16(const float* p, float (&v)[NT]) {
-  const float4* q = reinterpret_cast<const float4*>(p);
-#pragma unroll
-  for (int i = 0; i < NT / 4; ++i) {
-    const float4 w = q[i];
-    v[4 * i] = w.x; v[4 * i + 1] = w.y; v[4 * i + 2] = w.z; v[4 * i + 3] = w.w;
-  }
-}
-template <int NT>
-__device__ __forceinline__ void load_row16(const bf16_t* p, float (&v)[NT]) {
-  static_assert(NT % 4 == 0, "");
-  const uint2* q = reinterpret_cast<const uint2*>(p);  // 4 bf16 per 8 bytes
-#pragma unroll
-  for (int i = 0; i < NT / 4; ++i) {
-    const uint2 w = q[i];
-    v[4 * i] = __uint_as_float(w.x << 16);
-    v[4 * i + 1] = __uint_as_float(w.x & 0xffff0000u);
-    v[4 * i + 2] = __uint_as_float(w.y << 16);
-    v[4 * i + 3] = __uint_as_float(w.y & 0xffff0000u);
-  }
-}
-
-// dstate in {4, 8, 16}: one lane per (sequence, channel).  A block's state
-// tile (256 channels x N floats, contiguous in memory) moves between HBM and
-// LDS with fully coalesced 16-byte accesses; each lane then works on its own
-// channel's row from LDS, so softplus, the gate and the exponentials are
-// computed once per channel.  When the channel's A has the S4D-real shape
-// A[n] = (n+1) A[0], the decays are powers of r = e^(Delta A[0]) taken
-// against r's two-float value (one accurate exponential per channel).
-constexpr int kDecBlock = 256;
-template <typename TA, int NT>
-__global__ void __launch_bounds__(kDecBlock) decode_chan_kernel(DecArgs<TA> a) {
-  static_assert(NT % 4 == 0 && NT <= 16, "whole float4 rows");
-  constexpr int Q = NT / 4;            // float4 per row
-  constexpr int ROW = NT + 4;          // LDS row stride in floats (padding spreads banks)
-  __shared__ float4 tile[kDecBlock * ROW / 4];
-  const int64_t nch = a.batch * a.dim;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kDecBlock;
-  const int t = threadIdx.x;
-  const int nrows = static_cast<int>((nch - c0) < kDecBlock ? (nch - c0) : kDecBlock);
-  const float4* gst = reinterpret_cast<const float4*>(a.state + c0 * NT);
-  // coalesced load of the tile: float4 f = row f/Q, quad f%Q
-#pragma unroll
-  for (int k = 0; k < Q; ++k) {
-    const int f = t + k * kDecBlock;
-    if (f < nrows * Q) tile[(f / Q) * (ROW / 4) + (f % Q)] = gst[f];
-  }
-  __syncthreads();
-  const bool valid = t < nrows;
-  const int64_t c = c0 + (valid ? t : 0);
-  const int64_t b = c / a.dim;
-  const int d = static_cast<int>(c % a.dim);
-  float h[NT], Av[NT], Bv[NT], Cv[NT];
-  const float4* ap = reinterpret_cast<const float4*>(a.A + static_cast<size_t>(d) * NT);
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const float4 v = tile[t * (ROW / 4) + q];
-    const float4 w = ap[q];
-    h[4 * q] = v.x; h[4 * q + 1] = v.y; h[4 * q + 2] = v.z; h[4 * q + 3] = v.w;
-    Av[4 * q] = w.x; Av[4 * q + 1] = w.y; Av[4 * q + 2] = w.z; Av[4 * q + 3] = w.w;
-  }
-  // B and C rows of this sequence with 16-byte loads (rows are 16-byte aligned)
-  load_row16<NT>(a.B + b * NT, Bv);
-  load_row16<NT>(a.C + b * NT, Cv);
-  const float xv = to_f32(a.x[c]);
-  const float raw = to_f32(a.delta[c]) + (a.bias ? a.bias[d] : 0.0f);
-  const float dt = a.softplus ? softplus_f32(raw) : raw;
-  const float dx = dt * xv;
-  bool pow_ok = true;
-#pragma unroll
-  for (int n = 1; n < NT; ++n) pow_ok = pow_ok && (Av[n] == static_cast<float>(n + 1) * Av[0]);
-  float y = 0.0f;
-  if (__all(pow_ok)) {
-    float rl;
-    const float rh = exp_acc(dt * Av[0], rl);
-    float p = rh;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      h[n] = __builtin_fmaf(p, h[n], dx * Bv[n]);
-      y = __builtin_fmaf(Cv[n], h[n], y);
-      if (n + 1 < NT) p = __builtin_fmaf(p, rh, p * rl);
-    }
-  } else {
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      float unused;
-      h[n] = __builtin_fmaf(exp_acc(dt * Av[n], unused), h[n], dx * Bv[n]);
-      y = __builtin_fmaf(Cv[n], h[n], y);
-    }
-  }
-  y += (a.Dsk ? a.Dsk[d] : 0.0f) * xv;
-  if (a.z) y *= silu_f32(to_f32(a.z[c]));
-  if (valid) store_act(a.out + c, y);
-#pragma unroll
-  for (int q = 0; q < Q; ++q)
-    tile[t * (ROW / 4) + q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
-  __syncthreads();
-  float4* gso = reinterpret_cast<float4*>(a.state + c0 * NT);
-#pragma unroll
-  for (int k = 0; k < Q; ++k) {
-    const int f = t + k * kDecBlock;
-    if (f < nrows * Q) gso[f] = tile[(f / Q) * (ROW / 4) + (f % Q)];
   }
 }
 
@@ -570,23 +507,18 @@ int dispatch_fwd(const FwdArgs<TA>& a, int64_t batch, bool sp, hipStream_t s) {
 template <typename TA>
 int dispatch_decode(const DecArgs<TA>& a, hipStream_t s) {
   const int64_t nch = a.batch * a.dim;
-  auto vec = [&](auto kern, int G) {
+  auto quad = [&](auto kern, int G) {
     const int64_t threads = nch * G;
     const unsigned blocks = static_cast<unsigned>((threads + 255) / 256);
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, a);
     return launch_status("ssm_state_update");
   };
-  auto chan = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((nch + kDecBlock - 1) / kDecBlock)),
-                       dim3(kDecBlock), 0, s, a);
-    return launch_status("ssm_state_update");
-  };
   switch (a.N) {
-    case 4: return chan(decode_chan_kernel<TA, 4>);
-    case 8: return chan(decode_chan_kernel<TA, 8>);
-    case 16: return chan(decode_chan_kernel<TA, 16>);
-    case 32: return vec(decode_vec_kernel<TA, 8>, 8);
-    case 64: return vec(decode_vec_kernel<TA, 16>, 16);
+    case 4: return quad(decode_quad_kernel<TA, 1>, 1);
+    case 8: return quad(decode_quad_kernel<TA, 2>, 2);
+    case 16: return quad(decode_quad_kernel<TA, 4>, 4);
+    case 32: return quad(decode_quad_kernel<TA, 8>, 8);
+    case 64: return quad(decode_quad_kernel<TA, 16>, 16);
     default: {
       const unsigned blocks = static_cast<unsigned>((nch + 255) / 256);
       hipLaunchKernelGGL((decode_scalar_kernel<TA>), dim3(blocks), dim3(256), 0, s, a);
@@ -598,6 +530,7 @@ int dispatch_decode(const DecArgs<TA>& a, hipStream_t s) {
 constexpr int64_t kMaxDim = (int64_t{1} << 24);   // rows of a token group stay < 4 GiB
 constexpr int64_t kMaxLen = (int64_t{1} << 31) - 64;
 constexpr int64_t kMaxSeqs = (int64_t{1} << 24);  // packed sequences per call
+constexpr int64_t kMaxDecodeLanes = (int64_t{1} << 31) - 256;  // lanes of one decode launch
 
 // Checks and launch shared by both forward entry points.  Dense layout:
 // `batch` sequences of `seqlen` tokens, cu == NULL.  Packed layout: one row
@@ -761,8 +694,15 @@ int ssm_state_update(float* state, const void* x, const void* delta, const float
   if (dstate < 1 || dstate > 64)
     return fail(SSM_ERR_UNSUPPORTED, "ssm_state_update: dstate must be in [1, 64], got %lld",
                 (long long)dstate);
-  if (batch * dim * 16 > (int64_t{1} << 40))
-    return fail(SSM_ERR_SHAPE, "ssm_state_update: batch*dim too large");
+  // one lane per channel (per 4 states when dstate % 4 == 0): the lane count
+  // must fit one launch (grid size in work-items below 2^31)
+  const int64_t lanes_per_ch = dstate % 4 == 0 ? dstate / 4 : 1;
+  if (batch > kMaxDecodeLanes || dim > kMaxDecodeLanes ||
+      batch * dim > kMaxDecodeLanes / lanes_per_ch)
+    return fail(SSM_ERR_SHAPE,
+                "ssm_state_update: batch %lld x dim %lld x %lld lanes per channel exceeds %lld lanes",
+                (long long)batch, (long long)dim, (long long)lanes_per_ch,
+                (long long)kMaxDecodeLanes);
   if (!state || !x || !delta || !A || !B || !C || !out)
     return fail(SSM_ERR_NULL, "ssm_state_update: state, x, delta, A, B, C and out are required");
   const size_t es = dtype == SSM_DTYPE_F32 ? 4 : 2;
