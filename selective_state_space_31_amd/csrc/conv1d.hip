@@ -51,6 +51,12 @@ struct ConvArgs {
 
 // V activations moved as one 16-byte access (V > 1) or one element: the raw
 // bits are kept (fewer registers for a window of them) and widened at use.
+// Output rows are written once and not read again here, so the vector stores
+// carry the nontemporal hint (130M-shaped forward: 17.8 -> 14.1 us).  The
+// input loads do not: neighbouring stretches re-read 3 rows through L2.
+typedef float f32x4_e __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_e __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_e __attribute__((ext_vector_type(2)));
 template <typename TA, int V>
 struct VecIo;
 template <>
@@ -62,7 +68,7 @@ struct VecIo<float, 4> {
   }
   __device__ static raw_t from(const float (&v)[4]) { return make_float4(v[0], v[1], v[2], v[3]); }
   __device__ static void store(float* p, const float (&v)[4]) {
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    __builtin_nontemporal_store(f32x4_e{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4_e*>(p));
   }
 };
 // bf16: V = 2, 4 or 8 values in one 4-, 8- or 16-byte access.
@@ -102,11 +108,12 @@ struct VecBf16 {
   __device__ static void store(bf16_t* p, const float (&v)[V]) {
     const raw_t r = from(v);
     if constexpr (NW == 4) {
-      *reinterpret_cast<uint4*>(p) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+      __builtin_nontemporal_store(u32x4_e{r.w[0], r.w[1], r.w[2], r.w[3]},
+                                  reinterpret_cast<u32x4_e*>(p));
     } else if constexpr (NW == 2) {
-      *reinterpret_cast<uint2*>(p) = make_uint2(r.w[0], r.w[1]);
+      __builtin_nontemporal_store(u32x2_e{r.w[0], r.w[1]}, reinterpret_cast<u32x2_e*>(p));
     } else {
-      *reinterpret_cast<uint32_t*>(p) = r.w[0];
+      __builtin_nontemporal_store(r.w[0], reinterpret_cast<uint32_t*>(p));
     }
   }
 };

@@ -37,6 +37,10 @@ __device__ __forceinline__ void store_act(bf16_t* p, float v) {
 // offset: no per-access vector address arithmetic.
 using rsrc_t = __amdgpu_buffer_rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) 32-bit access, gfx9 family
+// Cache-policy operand of the buffer stores of per-token outputs: the
+// nontemporal bit (written once, never read back by the kernel that writes
+// them; ~1.5% on the forward).
+constexpr int kStoreStream = 2;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
@@ -54,7 +58,7 @@ struct Io<float> {
   }
   __device__ static float f32(raw_t v) { return __uint_as_float(v); }
   __device__ static void store(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, kStoreStream);
   }
 };
 template <>
@@ -67,7 +71,7 @@ struct Io<bf16_t> {
   __device__ static float f32(raw_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
   __device__ static void store(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
     __bf16 b = static_cast<__bf16>(v);  // round to nearest even
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, b), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, b), r, voff, soff, kStoreStream);
   }
 };
 

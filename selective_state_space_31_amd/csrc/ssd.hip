@@ -565,7 +565,7 @@ ssd_fwd_kernel(SsdArgs a) {
         }
         const u32x4 o = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
                          pack_bf16(y[6], y[7])};
-        __builtin_amdgcn_raw_buffer_store_b128(o, rO, vo_r, (16 * w + 8 * i) * rowX, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(o, rO, vo_r, (16 * w + 8 * i) * rowX, kStoreStream);
       }
       if constexpr (GATE) fetch_z(c + 1);
     }
