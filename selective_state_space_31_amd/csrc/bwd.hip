@@ -547,8 +547,23 @@ __global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(const float* __restr
                                                            int tiles) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= per) return;
+  // tile order; the loads of four tiles are issued before their adds
   float sb = 0.0f, scv = 0.0f;
-  for (int k = 0; k < tiles; ++k) {
+  int k = 0;
+  for (; k + 4 <= tiles; k += 4) {
+    float vb[4], vc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      vb[u] = pB[(k + u) * per + i];
+      vc[u] = pC[(k + u) * per + i];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sb += vb[u];
+      scv += vc[u];
+    }
+  }
+  for (; k < tiles; ++k) {
     sb += pB[k * per + i];
     scv += pC[k * per + i];
   }
@@ -560,7 +575,7 @@ __global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(const float* __restr
 // of 256 = 32 elements x 8 slice groups: group j sums the slices j, j+8, ...
 // in order, and the 8 group sums are added in order (a fixed order: the
 // result does not depend on scheduling).
-constexpr int kRedElems = 32, kRedGroups = 8;
+constexpr int kRedElems = 32, kRedGroups = 8, kRedBatch = 8;
 __global__ void __launch_bounds__(256) bwd_reduce_params_kernel(
     const float* __restrict__ pA, const float* __restrict__ pD, const float* __restrict__ pbias,
     float* __restrict__ dA, float* __restrict__ dD, float* __restrict__ dbias, int dim, int N,
@@ -569,12 +584,37 @@ __global__ void __launch_bounds__(256) bwd_reduce_params_kernel(
   const int e = threadIdx.x % kRedElems, j = threadIdx.x / kRedElems;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kRedElems + e;
   const int64_t nA = static_cast<int64_t>(dim) * N;
+  // slice order within the group; the loads of kRedBatch slices are issued
+  // before their adds (the latency of one load per add bound this loop)
   float v = 0.0f, vb = 0.0f;
+  constexpr int U = kRedBatch;
   if (i < nA) {
-    for (int64_t k = j; k < slices; k += kRedGroups) v += pA[k * nA + i];
+    int64_t k = j;
+    for (; k + (U - 1) * kRedGroups < slices; k += U * kRedGroups) {
+      float t[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) t[u] = pA[(k + u * kRedGroups) * nA + i];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v += t[u];
+    }
+    for (; k < slices; k += kRedGroups) v += pA[k * nA + i];
   } else if (i < nA + dim) {
     const int64_t d = i - nA;
-    for (int64_t k = j; k < slices; k += kRedGroups) {
+    int64_t k = j;
+    for (; k + (U - 1) * kRedGroups < slices; k += U * kRedGroups) {
+      float t[U], tb[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        t[u] = pD[(k + u * kRedGroups) * dim + d];
+        tb[u] = pbias[(k + u * kRedGroups) * dim + d];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        v += t[u];
+        vb += tb[u];
+      }
+    }
+    for (; k < slices; k += kRedGroups) {
       v += pD[k * dim + d];
       vb += pbias[k * dim + d];
     }
