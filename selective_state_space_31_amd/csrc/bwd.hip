@@ -366,7 +366,9 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
   };
 
   // one forward token (row i of the sub-chunk): h <- e^(dt A) h + dt B x; returns dt
-  auto fwd_step = [&](const Rows& r, int i, float (&hh)[SPL]) {
+  // (hout = e^(dt A) hin + dt B x, written to its own registers so that the
+  // sub-chunk recompute fills its history without copies)
+  auto fwd_step_to = [&](const Rows& r, int i, const float (&hin)[SPL], float (&hout)[SPL]) {
     const uint32_t so = static_cast<uint32_t>(i) * rowA;
     const float u = IO::f32(IO::load(r.delta, vo_a, so)) + bias;
     const float dt = SP ? softplus_f32(u) : u;
@@ -375,9 +377,10 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
     loadS(r.B, static_cast<uint32_t>(i) * rowN, Bv);
     decays(dt, dA);
 #pragma unroll
-    for (int j = 0; j < SPL; ++j) hh[j] = __builtin_fmaf(dA[j], hh[j], dx * Bv[j]);
+    for (int j = 0; j < SPL; ++j) hout[j] = __builtin_fmaf(dA[j], hin[j], dx * Bv[j]);
     return dt;
   };
+  auto fwd_step = [&](const Rows& r, int i, float (&hh)[SPL]) { return fwd_step_to(r, i, hh, hh); };
 
   // 4a. forward over the stripe with a checkpoint every SUB tokens (in LDS:
   // each lane reads back only its own); the state after the last sub-chunk
@@ -430,24 +433,26 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
     {
 #pragma unroll
       for (int j = 0; j < SPL; ++j) ck[j] = ckpt[k][j][tid];
-      float hc[SPL];
-#pragma unroll
-      for (int j = 0; j < SPL; ++j) hc[j] = ck[j];
 #pragma unroll
       for (int i = 0; i < SUB; ++i) {
-        dts[i] = 0.0f;
-        if (t0 + i < e) dts[i] = fwd_step(r, i, hc);
+        const float(&hin)[SPL] = i == 0 ? ck : hist[i > 0 ? i - 1 : 0];
+        if (t0 + i < e) {
+          dts[i] = fwd_step_to(r, i, hin, hist[i]);
+        } else {
+          dts[i] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < SPL; ++j) hist[i][j] = hc[j];
+          for (int j = 0; j < SPL; ++j) hist[i][j] = hin[j];
+        }
       }
     }
 #pragma unroll
     for (int i = SUB - 1; i >= 0; --i) {
       const int t = t0 + i;
-      float pv[V];
-#pragma unroll
-      for (int j = 0; j < V; ++j) pv[j] = 0.0f;
+      // rows past the stripe's end (the last stripe of a ragged length) are
+      // skipped: the adjoint passes through them unchanged, and the
+      // workgroup's sum below reads no dB / dC slot of theirs
       if (t < e) {
+        float pv[V];
         const uint32_t so = static_cast<uint32_t>(i) * rowA, son = static_cast<uint32_t>(i) * rowN;
         const float u = IO::f32(IO::load(r.delta, vo_a, so)) + bias;
         const float dt = dts[i];
@@ -494,9 +499,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
         if constexpr (GATE) IO::store(dzv, rdz, vo_st, so);
         dDacc = __builtin_fmaf(dy, xv, dDacc);
         dbacc += dd;
-      }
-      // dB, dC of this token: sum over the wave's channels
-      {
+        // dB, dC of this token: sum over the wave's channels
         const float w = reduce_scatter<V, G>(pv);
         if ((lane & (64 / V - 1) & ~(G - 1)) == 0) {
           const int vi = scatter_index<V>(lane);
