@@ -371,14 +371,21 @@ def cpu_baseline(W, torch):
     p = W.make_problem(**c, seed=0, device="cpu", engine="numpy")
     nthreads = oracle.oracle.default_threads()
     h = p.host_f32()
-    t = time.perf_counter()
-    oracle.scan(h["x"], h["delta"], h["A"], h["B"], h["C"], D=h["D"], z=h["z"],
-                delta_bias=h["delta_bias"], nthreads=nthreads)
-    dt = time.perf_counter() - t
-    toks = c["batch"] * c["L"] * c["dim"]
+    run = lambda: oracle.scan(h["x"], h["delta"], h["A"], h["B"], h["C"], D=h["D"], z=h["z"],
+                              delta_bias=h["delta_bias"], nthreads=nthreads)
+    # the batch again and again until about 10 s of CPU work (thread-seconds)
+    # have been timed, at most 30 s
+    reps, dt = 0, 0.0
+    while reps == 0 or (dt * nthreads < 10.0 and dt * nthreads * (reps + 1) / reps < 30.0):
+        t = time.perf_counter()
+        run()
+        dt += time.perf_counter() - t
+        reps += 1
+    toks = c["batch"] * c["L"] * c["dim"] * reps
     return dict(value=toks / dt, unit="tokens*channels/s", cores=nthreads, kind="oracle",
-                sample="one full batch: %d x %d tokens x %d channels, N=%d (%.2f s wall on %d threads)"
-                       % (c["batch"], c["L"], c["dim"], c["dstate"], dt, nthreads))
+                sample="%d passes over one full batch: %d x %d tokens x %d channels, N=%d "
+                       "(%.2f s wall on %d threads)"
+                       % (reps, c["batch"], c["L"], c["dim"], c["dstate"], dt, nthreads))
 
 
 def traffic_entry(kernel_ms):
