@@ -100,6 +100,12 @@ def test_state_update_rejects_bad_arguments(lib):
     assert lib.ssm_state_update(f(7), f(1), f(2), None, 1, f(3), f(4), f(5), None, None,
                                 P(0x11000000 + 4), 2, 64, 16, 0, None) == -5
     assert b"overlaps" in lib.ssm_last_error()
+    # one launch holds fewer than 2^31 - 256 lanes (dstate / 4 per channel here)
+    assert lib.ssm_state_update(f(7), f(1), f(2), None, 1, f(3), f(4), f(5), None, None, f(6),
+                                1 << 16, 1 << 13, 16, 0, None) == -2
+    assert b"lanes" in lib.ssm_last_error()
+    assert lib.ssm_state_update(f(7), f(1), f(2), None, 1, f(3), f(4), f(5), None, None, f(6),
+                                1 << 40, 1, 3, 0, None) == -2
 
 
 def _fwd_varlen(lib, **kw):
