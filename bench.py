@@ -60,8 +60,8 @@ def kernel_source_hash():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = enough to exceed 4x MALL)")
@@ -88,14 +88,17 @@ def sleep_cycles_per_ms(torch):
 
 
 def time_launches(fn, args_list, warmup, steps, torch):
-    """Run fn(*args_list[i % R]) warmup+steps times; events bracket each timed
-    launch on the stream the kernel runs on (torch's current stream).
+    """Run fn(*args_list[i % R]) warmup times, then time exactly `steps`
+    calls on the stream the kernels run on (torch's current stream).
 
-    The timed launches are enqueued behind a short device-side spin, sized to
-    outlast the host's time to enqueue them all, so the steps then run back
-    to back on the GPU: the events measure device time, not the Python
-    binding's per-call host overhead (which exceeds the shorter kernels).
-    Returns (total_ms, per-launch ms list)."""
+    The timed calls are enqueued behind a short device-side spin, sized to
+    outlast the host's time to enqueue them all, so they run back to back on
+    the GPU and the two events around them measure device time, not the
+    Python binding's per-call host overhead (which exceeds the shorter
+    kernels).  A second pass brackets every call with its own event pair: the
+    per-call spread, at the price of the markers between the calls (a few
+    microseconds each), which the first pass does not pay.
+    Returns (total_ms of the first pass, per-call ms list of the second)."""
     stream = torch.cuda.current_stream()
     R = len(args_list)
     for i in range(warmup):
@@ -106,18 +109,30 @@ def time_launches(fn, args_list, warmup, steps, torch):
         fn(*args_list[i % R])
     host_ms_per_call = (time.perf_counter() - t) * 1e3 / min(R, 8)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    spin = int(sleep_cycles_per_ms(torch) * (2.0 * host_ms_per_call * steps + 1.0))
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(sleep_cycles_per_ms(torch) * (2.0 * host_ms_per_call * steps + 1.0)))
+    torch.cuda._sleep(spin)
     t0.record(stream)
+    for i in range(steps):
+        fn(*args_list[(warmup + i) % R])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda._sleep(spin)
     for i in range(steps):
         ev[i][0].record(stream)
         fn(*args_list[(warmup + i) % R])
         ev[i][1].record(stream)
-    t1.record(stream)
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in ev]
+    return total_ms, [a.elapsed_time(b) for a, b in ev]
+
+
+def bracketed(per):
+    """Summary of the per-call event brackets (second pass)."""
+    per = sorted(per)
+    return dict(bracketed_call_ms_avg=sum(per) / len(per), bracketed_call_ms_median=per[len(per) // 2])
 
 
 def fwd_case(name, steps, warmup, replicas, torch, ops, W, seed=0):
@@ -135,13 +150,11 @@ def fwd_case(name, steps, warmup, replicas, torch, ops, W, seed=0):
         ops.ssm_scan_fwd(**p.tensors(), out=o, last_state=l)
 
     total_ms, per = time_launches(call, list(zip(probs, outs, lasts)), warmup, steps, torch)
-    per.sort()
-    ms = total_ms / steps
-    kern_ms = sum(per) / len(per)
+    ms = kern_ms = total_ms / steps
     toks = c["batch"] * c["L"] * c["dim"]
     res = dict(workload=name, batch=c["batch"], seq_len=c["L"], dim=c["dim"], dstate=c["dstate"],
                dtype=c["dtype"], gate=c["gate"], last_state=c["last_state"], input_replicas=R,
-               ms_per_step=ms, kernel_ms_avg=kern_ms, kernel_ms_median=per[len(per) // 2],
+               ms_per_step=ms, kernel_ms_avg=kern_ms, **bracketed(per),
                tokens_channels_per_s=toks / (ms * 1e-3), algorithmic_bytes=alg,
                achieved_GBps=alg / (kern_ms * 1e-3) / 1e9)
     res["pct_of_hbm_peak"] = 100.0 * res["achieved_GBps"] / HBM_PEAK_GBPS
@@ -171,12 +184,11 @@ def varlen_case(name, steps, warmup, torch, ops, W, seed=0):
         ops.ssm_scan_fwd_varlen(**p.tensors(), out=o, last_state=l)
 
     total_ms, per = time_launches(call, list(zip(probs, outs, lasts)), warmup, steps, torch)
-    ms = total_ms / steps
-    kern_ms = sum(per) / len(per)
+    ms = kern_ms = total_ms / steps
     toks = c["total"] * c["dim"]
     res = dict(workload=name, total_tokens=c["total"], nseq=nseq, lengths=lengths, dim=c["dim"],
                dstate=c["dstate"], dtype=c["dtype"], gate=c["gate"], last_state=True,
-               input_replicas=R, ms_per_step=ms, kernel_ms_avg=kern_ms,
+               input_replicas=R, ms_per_step=ms, kernel_ms_avg=kern_ms, **bracketed(per),
                tokens_channels_per_s=toks / (ms * 1e-3), algorithmic_bytes=alg,
                achieved_GBps=alg / (kern_ms * 1e-3) / 1e9)
     res["pct_of_hbm_peak"] = 100.0 * res["achieved_GBps"] / HBM_PEAK_GBPS
@@ -217,11 +229,11 @@ def conv_case(name, steps, warmup, torch, ops, W):
         def call(st, x):
             ops.ssm_causal_conv1d_update(st, x, p.weight, p.bias, out=out)
     total_ms, per = time_launches(call, args, warmup, steps, torch)
-    kern_ms = sum(per) / len(per)
+    kern_ms = total_ms / steps
     gbps = alg / (kern_ms * 1e-3) / 1e9
     res = dict(workload=name, batch=c["batch"], seq_len=c["L"], dim=c["dim"], width=c["width"],
                dtype=c["dtype"], silu=True, input_replicas=R, ms_per_step=total_ms / steps,
-               kernel_ms_avg=kern_ms, algorithmic_bytes=alg,
+               kernel_ms_avg=kern_ms, **bracketed(per), algorithmic_bytes=alg,
                tokens_channels_per_s=c["batch"] * c["L"] * c["dim"] / (kern_ms * 1e-3),
                roofline=dict(bound="hbm", achieved=round(gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                              frac=round(gbps / HBM_PEAK_GBPS, 4)))
@@ -261,10 +273,10 @@ def bwd_case(name, steps, warmup, torch, ops, W, seed=0):
                          grads=gr, workspace=ws)
 
     total_ms, per = time_launches(call, list(zip(probs, douts, grads)), warmup, steps, torch)
-    kern_ms = sum(per) / len(per)
+    kern_ms = total_ms / steps
     res = dict(workload=name + " backward", batch=c["batch"], seq_len=c["L"], dim=c["dim"],
                dstate=c["dstate"], dtype=c["dtype"], input_replicas=R,
-               ms_per_step=total_ms / steps, kernel_ms_avg=kern_ms,
+               ms_per_step=total_ms / steps, kernel_ms_avg=kern_ms, **bracketed(per),
                tokens_channels_per_s=tc / (kern_ms * 1e-3), algorithmic_bytes=alg,
                achieved_GBps=alg / (kern_ms * 1e-3) / 1e9)
     del probs, douts, grads, ws
@@ -298,12 +310,12 @@ def ssd_case(name, steps, warmup, torch, ops, W, seed=0):
         ops.ssm_ssd_fwd(p.x, p.dt, p.A, p.B, p.C, D=p.D, z=p.z, dt_bias=p.dt_bias, out=o)
 
     total_ms, per = time_launches(call, list(zip(probs, outs)), warmup, steps, torch)
-    kern_ms = sum(per) / len(per)
+    kern_ms = total_ms / steps
     tf = flops / (kern_ms * 1e-3) / 1e12
     gbps = alg / (kern_ms * 1e-3) / 1e9
     res = dict(workload=name, batch=c["batch"], seq_len=c["L"], nheads=c["H"], headdim=c["P"],
                dstate=c["N"], ngroups=c["G"], gate=c["gate"], dtype="bf16", input_replicas=R,
-               ms_per_step=total_ms / steps, kernel_ms_avg=kern_ms,
+               ms_per_step=total_ms / steps, kernel_ms_avg=kern_ms, **bracketed(per),
                tokens_channels_per_s=tok * c["H"] * c["P"] / (kern_ms * 1e-3),
                algorithmic_flops=flops, algorithmic_bytes=alg,
                roofline_mfma=dict(bound="mfma", achieved=round(tf, 1), peak=MFMA_BF16_PEAK_TFLOPS,
@@ -335,7 +347,7 @@ def decode_case(steps, warmup, torch, ops, W):
     args = [(i % nsl, i % nlayer) for i in range(nsl * nlayer)]
     total_ms, per = time_launches(call, args, warmup, steps, torch)
     alg = W.decode_step_bytes(c["batch"], c["dim"], c["dstate"])
-    kern_ms = sum(per) / len(per)
+    kern_ms = total_ms / steps
     # the workload as stated: 1024 chained steps of one layer on the stream,
     # enqueued behind a device-side spin as in time_launches (device time),
     # and as the host paces them through the Python binding
@@ -354,7 +366,7 @@ def decode_case(steps, warmup, torch, ops, W):
     host_paced_ms = (time.perf_counter() - h0) * 1e3
     res = dict(workload="decode_fp32", batch=c["batch"], dim=c["dim"], dstate=c["dstate"],
                layers_rotated=nlayer, ms_per_step=total_ms / steps, kernel_ms_avg=kern_ms,
-               tokens_channels_per_s=c["batch"] * c["dim"] / (kern_ms * 1e-3),
+               **bracketed(per), tokens_channels_per_s=c["batch"] * c["dim"] / (kern_ms * 1e-3),
                algorithmic_bytes=alg, achieved_GBps=alg / (kern_ms * 1e-3) / 1e9,
                chain_1024_steps_ms=t0.elapsed_time(t1),
                chain_1024_steps_host_paced_ms=host_paced_ms)
@@ -459,7 +471,7 @@ def main():
         outs = [torch.empty_like(p.x) for p in probs]
         tot, per = time_launches(lambda p, o: ops.ssm_scan_fwd(**p.tensors(), out=o),
                                  list(zip(probs, outs)), 5, max(10, a.steps // 2), torch)
-        kms = sum(per) / len(per)
+        kms = tot / max(10, a.steps // 2)
         secondary["mamba130m_bf16_general_A"] = dict(
             workload="mamba130m_bf16 with a non-structured A (every decay is its own exp)",
             kernel_ms_avg=kms,
