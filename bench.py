@@ -87,46 +87,64 @@ def sleep_cycles_per_ms(torch):
     return _sleep_cycles_per_ms
 
 
+PREROLL_MS = 10.0  # device time of untimed calls right before a timed region
+
+
 def time_launches(fn, args_list, warmup, steps, torch):
     """Run fn(*args_list[i % R]) warmup times, then time exactly `steps`
     calls on the stream the kernels run on (torch's current stream).
 
-    The timed calls are enqueued behind a short device-side spin, sized to
-    outlast the host's time to enqueue them all, so they run back to back on
-    the GPU and the two events around them measure device time, not the
-    Python binding's per-call host overhead (which exceeds the shorter
-    kernels).  A second pass brackets every call with its own event pair: the
-    per-call spread, at the price of the markers between the calls (a few
-    microseconds each), which the first pass does not pay.
+    The timed calls run back to back on the GPU and two events around them
+    measure device time, not the Python binding's per-call host time (which
+    exceeds the shorter kernels): they are enqueued behind a device-side spin
+    that outlasts the host's time to enqueue everything.  Between the spin and
+    the timed calls, untimed calls of the same workload keep the device busy
+    for about PREROLL_MS, so the timed region starts in the loaded steady
+    state (right after an idle spin, memory-bound kernels were measured up to
+    8% slower for the first milliseconds).  A second pass, set up the same
+    way, brackets every call with its own event pair: the per-call spread, at
+    the price of the markers between the calls (a few microseconds each),
+    which the first pass does not pay.
     Returns (total_ms of the first pass, per-call ms list of the second)."""
     stream = torch.cuda.current_stream()
     R = len(args_list)
     for i in range(warmup):
         fn(*args_list[i % R])
     torch.cuda.synchronize()
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t = time.perf_counter()
+    ea.record(stream)
     for i in range(min(R, 8)):
         fn(*args_list[i % R])
+    eb.record(stream)
     host_ms_per_call = (time.perf_counter() - t) * 1e3 / min(R, 8)
     torch.cuda.synchronize()
-    spin = int(sleep_cycles_per_ms(torch) * (2.0 * host_ms_per_call * steps + 1.0))
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(spin)
-    t0.record(stream)
-    for i in range(steps):
-        fn(*args_list[(warmup + i) % R])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda._sleep(spin)
-    for i in range(steps):
-        ev[i][0].record(stream)
-        fn(*args_list[(warmup + i) % R])
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    return total_ms, [a.elapsed_time(b) for a, b in ev]
+    dev_ms_per_call = max(ea.elapsed_time(eb) / min(R, 8), 1e-3)
+    pre = min(4000, max(warmup, int(PREROLL_MS / dev_ms_per_call) + 1))
+    spin = int(sleep_cycles_per_ms(torch) * (1.5 * host_ms_per_call * (pre + steps) + 1.0))
+
+    def region(bracket):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps if bracket else 0)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(spin)
+        for i in range(pre):
+            fn(*args_list[(warmup + i) % R])
+        t0.record(stream)
+        for i in range(steps):
+            if bracket:
+                ev[i][0].record(stream)
+            fn(*args_list[(warmup + pre + i) % R])
+            if bracket:
+                ev[i][1].record(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in ev]
+
+    total_ms, _ = region(False)
+    _, per = region(True)
+    return total_ms, per
 
 
 def bracketed(per):
@@ -349,11 +367,15 @@ def decode_case(steps, warmup, torch, ops, W):
     alg = W.decode_step_bytes(c["batch"], c["dim"], c["dstate"])
     kern_ms = total_ms / steps
     # the workload as stated: 1024 chained steps of one layer on the stream,
-    # enqueued behind a device-side spin as in time_launches (device time),
-    # and as the host paces them through the Python binding
+    # enqueued behind a device-side spin as in time_launches (device time;
+    # the untimed steps before it update the other layers' states), and as
+    # the host paces them through the Python binding
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(sleep_cycles_per_ms(torch) * (2.5 * c["steps"] * max(kern_ms, 0.05) + 5.0)))
+    pre = int(PREROLL_MS / max(kern_ms, 1e-3)) + 1
+    torch.cuda._sleep(int(sleep_cycles_per_ms(torch) * (2.5 * (c["steps"] + pre) * max(kern_ms, 0.05) + 5.0)))
+    for i in range(pre):
+        call(i % nsl, 1 + i % (nlayer - 1))
     t0.record()
     for s in range(c["steps"]):
         call(s % nsl, 0)
