@@ -272,6 +272,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
   constexpr int WAVES = kBwdThreads / 64;
   __shared__ float red[WAVES][SUB][2 * NT];
   __shared__ float ckpt[Sh::MAXSUB][SPL][kBwdThreads];  // per-lane checkpoints
+  constexpr bool kCacheDt = G > 1;
+  __shared__ float dtc[kCacheDt ? kBwdStripe : 1][kCacheDt ? CPB : 1];  // dt per token, channel
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -365,35 +367,50 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
     }
   };
 
-  // one forward token (row i of the sub-chunk): h <- e^(dt A) h + dt B x; returns dt
-  // (hout = e^(dt A) hin + dt B x, written to its own registers so that the
-  // sub-chunk recompute fills its history without copies)
-  auto fwd_step_to = [&](const Rows& r, int i, const float (&hin)[SPL], float (&hout)[SPL]) {
-    const uint32_t so = static_cast<uint32_t>(i) * rowA;
-    const float u = IO::f32(IO::load(r.delta, vo_a, so)) + bias;
-    const float dt = SP ? softplus_f32(u) : u;
-    const float dx = dt * IO::f32(IO::load(r.x, vo_a, so));
+  // dt of row i of the sub-chunk
+  auto step_dt = [&](const Rows& r, int i) {
+    const float u = IO::f32(IO::load(r.delta, vo_a, static_cast<uint32_t>(i) * rowA)) + bias;
+    return SP ? softplus_f32(u) : u;
+  };
+  // one forward token (row i of the sub-chunk): hout = e^(dt A) hin + dt B x
+  // (written to its own registers, so that the sub-chunk recompute fills its
+  // history without copies)
+  auto fwd_step_to = [&](const Rows& r, int i, float dt, const float (&hin)[SPL],
+                         float (&hout)[SPL]) {
+    const float dx = dt * IO::f32(IO::load(r.x, vo_a, static_cast<uint32_t>(i) * rowA));
     float Bv[SPL], dA[SPL];
     loadS(r.B, static_cast<uint32_t>(i) * rowN, Bv);
     decays(dt, dA);
 #pragma unroll
     for (int j = 0; j < SPL; ++j) hout[j] = __builtin_fmaf(dA[j], hin[j], dx * Bv[j]);
-    return dt;
   };
-  auto fwd_step = [&](const Rows& r, int i, float (&hh)[SPL]) { return fwd_step_to(r, i, hh, hh); };
 
   // 4a. forward over the stripe with a checkpoint every SUB tokens (in LDS:
   // each lane reads back only its own); the state after the last sub-chunk
-  // is not needed
+  // is not needed.  With several lanes per channel, every token's dt is also
+  // kept in LDS (both lanes write the same value; each reads it back), so
+  // the recompute below does not evaluate the softplus again.
   const int nsub = (len + SUB - 1) / SUB;
+  const int chw = tid / G;  // the lane's channel within the workgroup
   for (int k = 0; k < nsub; ++k) {
 #pragma unroll
     for (int j = 0; j < SPL; ++j) ckpt[k][j][tid] = h[j];
-    if (k == nsub - 1) break;
     const int t0 = s + k * SUB;
+    if (k == nsub - 1) {
+      if constexpr (kCacheDt) {
+        const Rows r = rows_at(t0, e);
+#pragma unroll 2
+        for (int i = 0; i < SUB; ++i) dtc[k * SUB + i][chw] = step_dt(r, i);
+      }
+      break;
+    }
     const Rows r = rows_at(t0, t0 + SUB);
 #pragma unroll 2
-    for (int i = 0; i < SUB; ++i) fwd_step(r, i, h);
+    for (int i = 0; i < SUB; ++i) {
+      const float dt = step_dt(r, i);
+      if constexpr (kCacheDt) dtc[k * SUB + i][chw] = dt;
+      fwd_step_to(r, i, dt, h, h);
+    }
   }
 
   // 4b. adjoint flowing into the stripe's last token from later tokens
@@ -437,7 +454,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
       for (int i = 0; i < SUB; ++i) {
         const float(&hin)[SPL] = i == 0 ? ck : hist[i > 0 ? i - 1 : 0];
         if (t0 + i < e) {
-          dts[i] = fwd_step_to(r, i, hin, hist[i]);
+          dts[i] = kCacheDt ? dtc[k * SUB + i][chw] : step_dt(r, i);
+          fwd_step_to(r, i, dts[i], hin, hist[i]);
         } else {
           dts[i] = 0.0f;
 #pragma unroll
