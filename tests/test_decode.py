@@ -58,6 +58,25 @@ def test_one_step_general_and_mixed_A(N, dtype):
     assert_close(to_np(state), ref_last, rtol, atol, "decode state")
 
 
+@pytest.mark.parametrize("N", [4, 8, 16, 64, 5])
+@pytest.mark.parametrize("shape", [(1, 1), (3, 7), (2, 33)], ids=lambda s: "b%d_d%d" % s)
+def test_one_step_tiny_shapes(N, shape):
+    """Launches whose last wave is mostly past the channels (1 channel: up to
+    63 idle lanes) and channel counts that are not a multiple of the wave's."""
+    batch, dim = shape
+    print("case: decode tiny b=%d d=%d N=%d" % (batch, dim, N), flush=True)
+    p = make_problem(batch, 1, dim, N, dtype="fp32", seed=50 + N + dim, device=DEV,
+                     initial_state=True)
+    state = p.h0.clone()
+    out = ssm_state_update(state, p.x[:, 0], p.delta[:, 0], p.A, p.B[:, 0], p.C[:, 0], D=p.D,
+                           z=p.z[:, 0], delta_bias=p.delta_bias)
+    torch.cuda.synchronize()
+    ref, ref_last = oracle_for(p)
+    rtol, atol = TOL["fp32"]
+    assert_close(to_np(out), ref[:, 0], rtol, atol, "decode out")
+    assert_close(to_np(state), ref_last, rtol, atol, "decode state")
+
+
 def test_one_step_equals_forward_with_L1():
     p = make_problem(3, 1, 130, 16, dtype="fp32", seed=31, device=DEV, initial_state=True)
     state = p.h0.clone()
