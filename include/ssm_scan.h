@@ -169,6 +169,8 @@ size_t ssm_scan_fwd_varlen_workspace_bytes(int64_t nseq, int64_t total_len, int6
  *     dinitial_state : (batch, dim, dstate) float32 or NULL
  *   dstate must be 4, 8 or 16 (SSM_ERR_UNSUPPORTED otherwise); alignment as
  *   ssm_scan_fwd, with B and C aligned to 4 elements and dB, dC to 16 bytes.
+ *   seqlen is at most 65535 * 32 = 2097120 (one launch holds the stripes of
+ *   32 tokens; SSM_ERR_SHAPE beyond).
  *   workspace: at least ssm_scan_bwd_workspace_bytes(...) bytes, 256-byte
  *   aligned (0 when seqlen is 0).
  * Arithmetic is float32; the sums over channels, tokens and sequences are

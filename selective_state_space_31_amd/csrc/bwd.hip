@@ -771,7 +771,7 @@ int dispatch_bwd(const BwdArgs<TA>& a, const FwdArgs<TA>& f, int N, bool sp, boo
 }
 
 constexpr int64_t kBwdMaxDim = int64_t{1} << 24;
-constexpr int64_t kBwdMaxLen = (int64_t{1} << 31) - 256;
+constexpr int64_t kBwdMaxLen = int64_t{65535} * kBwdStripe;  // stripes fill a grid dimension
 
 }  // namespace ssm
 

@@ -196,6 +196,7 @@ def _bwd(lib, **kw):
     (dict(z=ctypes.c_void_p(0x1c000000)), -1),          # z without dz
     (dict(dD=ctypes.c_void_p(0x1d000000)), -1),         # dD without D
     (dict(N=12), -3), (dict(N=32), -3), (dict(dtype=2), -3), (dict(batch=0), -2),
+    (dict(L=65535 * 32 + 1), -2),                       # more stripes than one launch holds
     (dict(dB=ctypes.c_void_p(0x1a000004)), -4),
     (dict(dx=ctypes.c_void_p(0x11000000 + 64)), -5),    # dx over x
     (dict(dC=ctypes.c_void_p(0x1a000000 + 256)), -5),   # dC over dB
@@ -210,6 +211,7 @@ def test_bwd_workspace_query(lib):
     assert lib.ssm_scan_bwd_workspace_bytes(4, 2048, 1536, 16, 1) > 0
     assert lib.ssm_scan_bwd_workspace_bytes(4, 2048, 1536, 12, 1) == 0
     assert lib.ssm_scan_bwd_workspace_bytes(4, 0, 1536, 16, 1) == 0
+    assert lib.ssm_scan_bwd_workspace_bytes(1, 65535 * 32 + 1, 64, 16, 1) == 0
 
 
 def _ssd(lib, **kw):
