@@ -266,7 +266,8 @@ int ssm_state_update(float* state, const void* x, const void* delta, const float
  *   final_conv_state   : (batch, dim, width-1) act or NULL; receives the last
  *                        width-1 inputs (exact copies), oldest first
  *   silu               : 1 = apply SiLU, 0 = the convolution alone
- *   2 <= width <= 4; batch, dim >= 1; seqlen >= 0.
+ *   2 <= width <= 4; batch, dim >= 1; seqlen >= 0; one launch holds
+ *   batch * ceil(seqlen / 16) * ceil(dim / 64) < 2^25 (SSM_ERR_SHAPE beyond).
  * Arithmetic is float32 (fused multiply-adds in tap order); bf16 outputs are
  * rounded to nearest even.  Outputs may not overlap inputs.
  */
@@ -280,6 +281,7 @@ int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
  *   conv_state : (batch, dim, width-1) act, read and shifted in place (the
  *                oldest input drops out, x becomes the newest)
  *   x, out     : (batch, dim) act;  weight, bias, silu, width, dtype as above.
+ *   batch * dim < 2^31 - 256 (one lane per channel in one launch).
  * Equivalent to ssm_causal_conv1d_fwd with seqlen = 1 and initial_conv_state
  * = final_conv_state = conv_state.
  */

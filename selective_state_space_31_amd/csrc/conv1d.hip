@@ -355,6 +355,10 @@ int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
       seqlen > (int64_t{1} << 40) / dim)
     return fail(SSM_ERR_SHAPE, "%s: bad sizes batch %lld, seqlen %lld, dim %lld", fn,
                 (long long)batch, (long long)seqlen, (long long)dim);
+  // one launch: at most 2^25 units of 64 lanes (counted for one channel per lane)
+  if (batch * ((seqlen + kConvTokens - 1) / kConvTokens) * ((dim + 63) / 64) >= (int64_t{1} << 25))
+    return fail(SSM_ERR_SHAPE, "%s: batch %lld x seqlen %lld x dim %lld exceeds one launch", fn,
+                (long long)batch, (long long)seqlen, (long long)dim);
   if (!weight || (seqlen > 0 && (!x || !out)))
     return fail(SSM_ERR_NULL, "%s: weight, x and out are required", fn);
   const size_t es = dtype == SSM_DTYPE_F32 ? 4 : 2;
@@ -415,7 +419,7 @@ int ssm_causal_conv1d_update(void* conv_state, const void* x, const float* weigh
     return fail(SSM_ERR_UNSUPPORTED, "%s: silu must be 0 or 1, got %d", fn, silu);
   if (width < 2 || width > 4)
     return fail(SSM_ERR_UNSUPPORTED, "%s: width must be 2, 3 or 4, got %lld", fn, (long long)width);
-  if (batch < 1 || dim < 1 || dim > kConvMaxDim || batch * dim > (int64_t{1} << 36))
+  if (batch < 1 || dim < 1 || dim > kConvMaxDim || batch * dim > (int64_t{1} << 31) - 256)
     return fail(SSM_ERR_SHAPE, "%s: bad sizes batch %lld, dim %lld", fn, (long long)batch,
                 (long long)dim);
   if (!conv_state || !x || !weight || !out)

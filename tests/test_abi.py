@@ -160,6 +160,7 @@ def _conv(lib, **kw):
     (dict(x=ctypes.c_void_p(0x11000001)), -4), (dict(w=ctypes.c_void_p(0x12000002)), -4),
     (dict(out=ctypes.c_void_p(0x11000000 + 64)), -5),
     (dict(s1=ctypes.c_void_p(0x13000000 + 32)), -5),
+    (dict(batch=65535, L=1 << 20, dim=64), -2),          # more units than one launch holds
 ])
 def test_conv_fwd_rejects_bad_arguments_before_launch(lib, kw, code):
     assert _conv(lib, **kw) == code
@@ -174,6 +175,9 @@ def test_conv_update_rejects_bad_arguments(lib):
     assert lib.ssm_causal_conv1d_update(f(4), f(1), f(2), None, f(3), 2, 64, 5, 1, 1, None) == -3
     assert lib.ssm_causal_conv1d_update(f(4), f(1), f(2), None, P(0x14000000 + 2), 2, 64, 4, 1, 1,
                                         None) == -5
+    # one lane per channel in one launch
+    assert lib.ssm_causal_conv1d_update(f(4), f(1), f(2), None, f(3), 1 << 16, 1 << 15, 4, 1, 1,
+                                        None) == -2
 
 
 def _bwd(lib, **kw):
