@@ -126,7 +126,7 @@ size_t ssm_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  *                      sequence's state after its last token (its initial
  *                      state if it is empty).  May not overlap initial_state.
  *   A, D_skip, delta_bias, delta_softplus, dtype : as in ssm_scan_fwd.
- *   1 <= nseq <= 2^24; total_len >= 0.
+ *   1 <= nseq < 2^24; total_len >= 0.
  *   workspace        : at least ssm_scan_fwd_varlen_workspace_bytes(...)
  *                      bytes, 256-byte aligned, as in ssm_scan_fwd.
  * Each sequence's out and last_state equal those of ssm_scan_fwd run on that
@@ -170,7 +170,8 @@ size_t ssm_scan_fwd_varlen_workspace_bytes(int64_t nseq, int64_t total_len, int6
  *   dstate must be 4, 8 or 16 (SSM_ERR_UNSUPPORTED otherwise); alignment as
  *   ssm_scan_fwd, with B and C aligned to 4 elements and dB, dC to 16 bytes.
  *   seqlen is at most 65535 * 32 = 2097120 (one launch holds the stripes of
- *   32 tokens; SSM_ERR_SHAPE beyond).
+ *   32 tokens), and batch * seqlen * dstate and batch * dim * dstate stay
+ *   below 2^31 - 256 (SSM_ERR_SHAPE beyond).
  *   workspace: at least ssm_scan_bwd_workspace_bytes(...) bytes, 256-byte
  *   aligned (0 when seqlen is 0).
  * Arithmetic is float32; the sums over channels, tokens and sequences are

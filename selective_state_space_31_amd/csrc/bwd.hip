@@ -772,6 +772,7 @@ int dispatch_bwd(const BwdArgs<TA>& a, const FwdArgs<TA>& f, int N, bool sp, boo
 
 constexpr int64_t kBwdMaxDim = int64_t{1} << 24;
 constexpr int64_t kBwdMaxLen = int64_t{65535} * kBwdStripe;  // stripes fill a grid dimension
+constexpr int64_t kBwdMaxLanes = (int64_t{1} << 31) - 256;
 
 }  // namespace ssm
 
@@ -783,7 +784,8 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
                                     int dtype) {
   (void)dtype;
   if (batch < 1 || batch > 65535 || dim < 1 || dim > kBwdMaxDim || seqlen < 0 ||
-      seqlen > kBwdMaxLen || (dstate != 4 && dstate != 8 && dstate != 16))
+      seqlen > kBwdMaxLen || (dstate != 4 && dstate != 8 && dstate != 16) ||
+      batch * seqlen * dstate > kBwdMaxLanes || batch * dim * dstate > kBwdMaxLanes)
     return 0;
   return bwd_layout(batch, seqlen, dim, dstate, plan_bwd(batch, seqlen, dim, dstate)).total;
 }
@@ -809,6 +811,11 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* delta_bias, int 
       seqlen > kBwdMaxLen)
     return fail(SSM_ERR_SHAPE, "%s: bad sizes batch %lld, seqlen %lld, dim %lld", fn,
                 (long long)batch, (long long)seqlen, (long long)dim);
+  // the one-lane-per-element passes (dB/dC sums, the states of an empty call)
+  if (batch * seqlen * dstate > kBwdMaxLanes || batch * dim * dstate > kBwdMaxLanes)
+    return fail(SSM_ERR_SHAPE, "%s: batch %lld x (seqlen %lld or dim %lld) x dstate %lld exceeds "
+                "one launch", fn, (long long)batch, (long long)seqlen, (long long)dim,
+                (long long)dstate);
   if (!A || !dA) return fail(SSM_ERR_NULL, "%s: A and dA are required", fn);
   if (seqlen > 0 && (!x || !delta || !B || !C || !dout || !dx || !ddelta || !dB || !dC))
     return fail(SSM_ERR_NULL, "%s: x, delta, B, C, dout, dx, ddelta, dB and dC are required", fn);

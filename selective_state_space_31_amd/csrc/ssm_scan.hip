@@ -529,7 +529,7 @@ int dispatch_decode(const DecArgs<TA>& a, hipStream_t s) {
 
 constexpr int64_t kMaxDim = (int64_t{1} << 24);   // rows of a token group stay < 4 GiB
 constexpr int64_t kMaxLen = (int64_t{1} << 31) - 64;
-constexpr int64_t kMaxSeqs = (int64_t{1} << 24);  // packed sequences per call
+constexpr int64_t kMaxSeqs = (int64_t{1} << 24) - 1;  // packed sequences per call (x 256 lanes < 2^32)
 constexpr int64_t kMaxDecodeLanes = (int64_t{1} << 31) - 256;  // lanes of one decode launch
 
 // Checks and launch shared by both forward entry points.  Dense layout:

@@ -123,7 +123,7 @@ def _fwd_varlen(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(cu=None), -1), (dict(x=None), -1), (dict(nseq=0), -2), (dict(nseq=(1 << 24) + 1), -2),
+    (dict(cu=None), -1), (dict(x=None), -1), (dict(nseq=0), -2), (dict(nseq=1 << 24), -2),
     (dict(T=-1), -2), (dict(N=65), -3), (dict(cu=ctypes.c_void_p(0x18000002)), -4),
     # last_state may not be initial_state for packed sequences
     (dict(last=ctypes.c_void_p(0x19000000), h0=ctypes.c_void_p(0x19000000)), -5),
@@ -201,6 +201,7 @@ def _bwd(lib, **kw):
     (dict(dD=ctypes.c_void_p(0x1d000000)), -1),         # dD without D
     (dict(N=12), -3), (dict(N=32), -3), (dict(dtype=2), -3), (dict(batch=0), -2),
     (dict(L=65535 * 32 + 1), -2),                       # more stripes than one launch holds
+    (dict(batch=4096, L=1 << 16), -2),                  # batch x seqlen x dstate lanes
     (dict(dB=ctypes.c_void_p(0x1a000004)), -4),
     (dict(dx=ctypes.c_void_p(0x11000000 + 64)), -5),    # dx over x
     (dict(dC=ctypes.c_void_p(0x1a000000 + 256)), -5),   # dC over dB
@@ -216,6 +217,7 @@ def test_bwd_workspace_query(lib):
     assert lib.ssm_scan_bwd_workspace_bytes(4, 2048, 1536, 12, 1) == 0
     assert lib.ssm_scan_bwd_workspace_bytes(4, 0, 1536, 16, 1) == 0
     assert lib.ssm_scan_bwd_workspace_bytes(1, 65535 * 32 + 1, 64, 16, 1) == 0
+    assert lib.ssm_scan_bwd_workspace_bytes(4096, 1 << 16, 64, 16, 1) == 0
 
 
 def _ssd(lib, **kw):
