@@ -446,7 +446,7 @@ def traffic_entry(kernel_ms):
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(--gpus %d requested); run with --gpus 1." % a.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
