@@ -1,25 +1,26 @@
 #!/usr/bin/env python3
 """Selective-scan benchmark on one MI355X.
 
-A step is one ssm_scan_fwd call over one batch of the Mamba-130M-shaped
-layer (batch 4, seq 2048, 1536 channels, N=16, bf16 activations, float32
-state, z gate on): every row of the hot path (softplus, decay, input term,
-recurrence, readout + skip, gate, store) runs in that one launch.  Inputs are
-resident in HBM before timing starts; each step reads a different replica of
-the inputs, and the replicas together are several times the 256 MB MALL, so
-steady-state steps stream from HBM rather than the last-level cache.
+A step is one ssm_scan_fwd call over one batch of the long-context layer
+(batch 1, 131072 tokens, 2048 channels, N=16, bf16 activations, float32
+state, no gate, dt log-uniform in [1e-4, 1e-1]): every row of the hot path
+(softplus, decay, input term, recurrence, readout + skip, store) runs in
+that call.  It is the largest single-GPU configuration of the metric, so it
+is the one the line reports.  Inputs (1.6 GB, several times the 256 MB MALL)
+are resident in HBM before timing starts.
 
-Prints ONE JSON line (the metric named on the config) with the roofline of
-the forward kernel and the float64 oracle timed on the host as a baseline,
-plus secondary records for the other workloads (2.8B-shaped layer,
-131k-token long context, the 130M-shaped layer with a general A, the same
-tokens as packed prompts of mixed lengths, one decode step, and the causal
-convolution before the scan: forward and decode update; the backward pass
-of the 130M-shaped layer; the SSD (Mamba-2) form of a 2.7B-shaped layer on
-the matrix cores).
+Prints ONE JSON line (the metric named on the config) with the HBM roofline
+of the call and its vector-ALU issue fraction (from the committed rocprofv3
+counters), the float64 oracle timed on the host over the same inputs as a
+baseline, and secondary records for the other workloads (the 130M- and
+2.8B-shaped layers, the 130M-shaped layer with a general A, the same tokens
+as packed prompts of mixed lengths, one decode step, the causal convolution
+before the scan: forward and decode update; the backward pass of the
+130M-shaped layer; the SSD (Mamba-2) form of a 2.7B-shaped layer on the
+matrix cores), each with its own roofline.
 
-  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
-                  [--no-secondary]
+  python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
+                  [--no-secondary] [--only WORKLOAD]
 """
 import argparse
 import hashlib
@@ -32,29 +33,61 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, vendor peak
-# non-packed fp32 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz
-VALU_PEAK_TFLOPS = 78.6
-# algorithmic work of the scan: per state element the decay (multiply + exp,
-# counted 1), the input term (multiply) and two FMAs (2 each); per token and
-# channel softplus, skip and gate (counted 10)
-FLOPS_PER_STATE_ELEMENT = 7
-FLOPS_PER_TOKEN_CHANNEL = 10
+# vector-ALU issue: a wave64 VALU instruction occupies a SIMD16 for 4 cycles,
+# so the chip issues at most 256 CUs x 4 SIMDs x 2.4 GHz / 4 wave instructions
+# per second (transcendentals take two such slots: counted twice)
+CUS, SIMDS_PER_CU, CLOCK_HZ = 256, 4, 2.4e9
+VALU_WAVE_INSTR_PEAK = CUS * SIMDS_PER_CU * CLOCK_HZ / 4.0
 MALL_BYTES = 256 << 20      # Infinity Cache (last-level) capacity
-WORKLOAD = "mamba130m_bf16"
+WORKLOAD = "longctx_bf16"
 METRIC = "selective-scan fwd tokens·channels/s + achieved HBM GB/s (% of peak), 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_mamba130m_bf16_traffic.json")
-KERNEL_SRCS = [os.path.join(ROOT, "selective_state_space_31_amd", "csrc", f)
-               for f in ("kernels.hpp", "ssm_scan.hip")]
+COUNTERS_DIR = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "selective_state_space_31_amd", "csrc")
 
 
 def kernel_source_hash():
-    """Hash of the forward kernels' sources, recorded with traffic counters so
-    that counters taken on other code are never reported."""
+    """Hash of the library's kernel sources, recorded with the rocprofv3
+    counters so that counters taken on other code are never reported."""
     h = hashlib.sha256()
-    for p in KERNEL_SRCS:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def counters_entry(workload):
+    """HBM bytes (FETCH_SIZE / WRITE_SIZE scaled by a copy of known size) and
+    VALU instructions per call of a workload, from
+    profiles/<workload>_counters.json, if they were taken on the kernel
+    sources as they are now; else None."""
+    try:
+        with open(os.path.join(COUNTERS_DIR, workload + "_counters.json")) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t
+
+
+def roofline(workload, alg_bytes, call_ms, kernels):
+    """HBM roofline of one call (all its launches): algorithmic bytes over the
+    call's time against 8 TB/s, with the counted HBM traffic and the VALU
+    issue fraction over the same time when counters on this code exist."""
+    gbps = alg_bytes / (call_ms * 1e-3) / 1e9
+    r = dict(bound="hbm", achieved=round(gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+             frac=round(gbps / HBM_PEAK_GBPS, 4), traffic=None, kernel=kernels,
+             algorithmic_bytes_per_launch=alg_bytes, kernel_ms_avg=round(call_ms, 5))
+    c = counters_entry(workload)
+    if c is not None:
+        r["traffic"] = c.get("hbm_bytes_per_call")
+        vi = c.get("valu_insts_per_call")
+        vt = c.get("valu_trans_insts_per_call", 0)
+        if vi:
+            r["valu_issue_frac"] = round((vi + vt) / (call_ms * 1e-3) / VALU_WAVE_INSTR_PEAK, 4)
+            r["valu_insts_per_call"] = vi
+    return r
 
 
 def parse():
@@ -176,7 +209,35 @@ def fwd_case(name, steps, warmup, replicas, torch, ops, W, seed=0):
                tokens_channels_per_s=toks / (ms * 1e-3), algorithmic_bytes=alg,
                achieved_GBps=alg / (kern_ms * 1e-3) / 1e9)
     res["pct_of_hbm_peak"] = 100.0 * res["achieved_GBps"] / HBM_PEAK_GBPS
+    res["roofline"] = roofline(name, alg, kern_ms, "one ssm_scan_fwd call (all its launches)")
     del probs, outs, lasts
+    torch.cuda.empty_cache()
+    return res
+
+
+def general_A_case(name, steps, warmup, torch, ops, W):
+    """A forward workload with a non-structured ("trained-like") A: every
+    decay is its own exponential."""
+    c = dict(W.CONFIGS[name])
+    dev = torch.device("cuda:0")
+    alg = W.algorithmic_bytes(c["batch"], c["L"], c["dim"], c["dstate"], c["dtype"], c["gate"],
+                              c["last_state"])
+    R = max(1, min(8, -(-4 * MALL_BYTES // alg)))
+    probs = [W.make_problem(**c, seed=r, device=dev, engine="torch_cuda", A_kind="general")
+             for r in range(R)]
+    outs = [torch.empty_like(p.x) for p in probs]
+    total_ms, per = time_launches(lambda p, o: ops.ssm_scan_fwd(**p.tensors(), out=o),
+                                  list(zip(probs, outs)), warmup, steps, torch)
+    kms = total_ms / steps
+    toks = c["batch"] * c["L"] * c["dim"]
+    res = dict(workload=name + " with a non-structured A (every decay its own exponential)",
+               batch=c["batch"], seq_len=c["L"], dim=c["dim"], dstate=c["dstate"],
+               dtype=c["dtype"], gate=c["gate"], input_replicas=R, ms_per_step=kms,
+               kernel_ms_avg=kms, **bracketed(per), tokens_channels_per_s=toks / (kms * 1e-3),
+               algorithmic_bytes=alg, achieved_GBps=alg / (kms * 1e-3) / 1e9,
+               roofline=roofline(name + "_general_A", alg, kms,
+                                 "one ssm_scan_fwd call (all its launches)"))
+    del probs, outs
     torch.cuda.empty_cache()
     return res
 
@@ -210,6 +271,7 @@ def varlen_case(name, steps, warmup, torch, ops, W, seed=0):
                tokens_channels_per_s=toks / (ms * 1e-3), algorithmic_bytes=alg,
                achieved_GBps=alg / (kern_ms * 1e-3) / 1e9)
     res["pct_of_hbm_peak"] = 100.0 * res["achieved_GBps"] / HBM_PEAK_GBPS
+    res["roofline"] = roofline(name, alg, kern_ms, "one ssm_scan_fwd_varlen call (all its launches)")
     del probs, outs, lasts
     torch.cuda.empty_cache()
     return res
@@ -296,7 +358,8 @@ def bwd_case(name, steps, warmup, torch, ops, W, seed=0):
                dstate=c["dstate"], dtype=c["dtype"], input_replicas=R,
                ms_per_step=total_ms / steps, kernel_ms_avg=kern_ms, **bracketed(per),
                tokens_channels_per_s=tc / (kern_ms * 1e-3), algorithmic_bytes=alg,
-               achieved_GBps=alg / (kern_ms * 1e-3) / 1e9)
+               achieved_GBps=alg / (kern_ms * 1e-3) / 1e9,
+               roofline=roofline(name + "_bwd", alg, kern_ms, "one ssm_scan_bwd call (all its launches)"))
     del probs, douts, grads, ws
     torch.cuda.empty_cache()
     return res
@@ -393,54 +456,51 @@ def decode_case(steps, warmup, torch, ops, W):
                chain_1024_steps_ms=t0.elapsed_time(t1),
                chain_1024_steps_host_paced_ms=host_paced_ms)
     res["pct_of_hbm_peak"] = 100.0 * res["achieved_GBps"] / HBM_PEAK_GBPS
+    res["roofline"] = roofline("decode_fp32", alg, kern_ms, "one ssm_state_update call")
     return res
 
 
 def cpu_baseline(W, torch):
     """The float64 oracle as it stands, on the host cores, over the same
-    workload: one whole batch of the 130M-shaped layer (all channels, all
-    tokens), from the same generator, bf16 values widened exactly."""
+    workload and the same input values as the GPU line: the long-context
+    layer's batch drawn by the same device generator and seed as the first
+    GPU input replica, copied to the host (bf16 values widened exactly).
+    One pass over the whole batch is about 20 thread-seconds of CPU work.
+    Threads: the host's CPU share for this GPU (its affinity set, at most 16,
+    the share one GPU of the box is sized for); the host's logical CPU count
+    is reported beside it."""
     import oracle
     c = dict(W.CONFIGS[WORKLOAD])
-    p = W.make_problem(**c, seed=0, device="cpu", engine="numpy")
-    nthreads = oracle.oracle.default_threads()
+    p = W.make_problem(**c, seed=0, device=torch.device("cuda:0"), engine="torch_cuda")
     h = p.host_f32()
-    run = lambda: oracle.scan(h["x"], h["delta"], h["A"], h["B"], h["C"], D=h["D"], z=h["z"],
-                              delta_bias=h["delta_bias"], nthreads=nthreads)
-    # the batch again and again until about 10 s of CPU work (thread-seconds)
-    # have been timed, at most 30 s
-    reps, dt = 0, 0.0
-    while reps == 0 or (dt * nthreads < 10.0 and dt * nthreads * (reps + 1) / reps < 30.0):
-        t = time.perf_counter()
-        run()
-        dt += time.perf_counter() - t
-        reps += 1
-    toks = c["batch"] * c["L"] * c["dim"] * reps
-    # one pass on a single thread, for the scaling over the host's cores
+    del p
+    torch.cuda.empty_cache()
+    nthreads = oracle.oracle.default_threads()
     t = time.perf_counter()
     oracle.scan(h["x"], h["delta"], h["A"], h["B"], h["C"], D=h["D"], z=h["z"],
-                delta_bias=h["delta_bias"], nthreads=1)
+                delta_bias=h["delta_bias"], nthreads=nthreads, want_last_state=False)
+    dt = time.perf_counter() - t
+    toks = c["batch"] * c["L"] * c["dim"]
+    # a single thread on 64 of the channels (whole sequence), for the scaling
+    sub = slice(0, 64)
+    t = time.perf_counter()
+    oracle.scan(h["x"][..., sub], h["delta"][..., sub], h["A"][sub], h["B"], h["C"],
+                D=h["D"][sub], z=None, delta_bias=h["delta_bias"][sub], nthreads=1,
+                want_last_state=False)
     dt1 = time.perf_counter() - t
-    return dict(value=toks / dt, unit="tokens*channels/s", cores=nthreads, kind="oracle",
-                sample="%d passes over one full batch: %d x %d tokens x %d channels, N=%d "
-                       "(%.2f s wall on %d threads)"
-                       % (reps, c["batch"], c["L"], c["dim"], c["dstate"], dt, nthreads),
-                single_thread=dict(value=c["batch"] * c["L"] * c["dim"] / dt1,
-                                   sample="one pass over the same batch (%.2f s)" % dt1))
-
-
-def traffic_entry(kernel_ms):
-    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE,
-    WRITE_SIZE, scaled by a copy-kernel calibration), if they were taken on
-    the kernel source as it is now; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
-        return None
-    return t.get("hbm_bytes_per_launch")
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return dict(value=toks / dt, unit="tokens*channels/s", cores=nthreads, kind="oracle",
+                host_logical_cpus=os.cpu_count(), host_affinity_cpus=affinity,
+                sample="one pass over the whole batch: %d x %d tokens x %d channels, N=%d, the "
+                       "GPU line's input values (device Philox, seed 0) copied to the host "
+                       "(%.2f s wall on %d threads)" % (c["batch"], c["L"], c["dim"], c["dstate"],
+                                                          dt, nthreads),
+                single_thread=dict(value=c["batch"] * c["L"] * 64 / dt1,
+                                   sample="channels 0-63 over the whole sequence on one thread "
+                                          "(%.2f s)" % dt1))
 
 
 def main():
@@ -474,7 +534,9 @@ def main():
             torch.cuda.synchronize()
             print(json.dumps({"copy_bytes_each_way": n * 4, "copies": a.steps}))
             return
-        if a.only == "decode_fp32":
+        if a.only.endswith("_general_A") and a.only[:-10] in W.CONFIGS:
+            print(json.dumps(general_A_case(a.only[:-10], a.steps, a.warmup, torch, ops, W)))
+        elif a.only == "decode_fp32":
             print(json.dumps(decode_case(a.steps, a.warmup, torch, ops, W)))
         elif a.only in W.VARLEN_CONFIGS:
             print(json.dumps(varlen_case(a.only, a.steps, a.warmup, torch, ops, W)))
@@ -490,27 +552,13 @@ def main():
     main_res = fwd_case(WORKLOAD, a.steps, a.warmup, a.replicas, torch, ops, W)
     secondary = {}
     if not a.no_secondary:
-        warm = fwd_case(WORKLOAD, a.steps, a.warmup, 1, torch, ops, W)
-        warm["workload"] = WORKLOAD + ", one input replica (the inputs stay in the 256 MB MALL: warm)"
+        secondary["mamba130m_bf16"] = fwd_case("mamba130m_bf16", a.steps, a.warmup, 0, torch, ops, W)
+        warm = fwd_case("mamba130m_bf16", a.steps, a.warmup, 1, torch, ops, W)
+        warm["workload"] = "mamba130m_bf16, one input replica (the inputs stay in the 256 MB MALL: warm)"
         secondary["mamba130m_bf16_warm"] = warm
         secondary["mamba2p8b_bf16"] = fwd_case("mamba2p8b_bf16", max(5, a.steps // 5), 3, 0, torch, ops, W)
-        secondary["longctx_bf16"] = fwd_case("longctx_bf16", max(3, a.steps // 10), 2, 0, torch, ops, W)
-        c = dict(W.CONFIGS[WORKLOAD])
-        dev = torch.device("cuda:0")
-        R = main_res["input_replicas"]
-        probs = [W.make_problem(**c, seed=r, device=dev, engine="torch_cuda", A_kind="general")
-                 for r in range(R)]
-        outs = [torch.empty_like(p.x) for p in probs]
-        tot, per = time_launches(lambda p, o: ops.ssm_scan_fwd(**p.tensors(), out=o),
-                                 list(zip(probs, outs)), 5, max(10, a.steps // 2), torch)
-        kms = tot / max(10, a.steps // 2)
-        secondary["mamba130m_bf16_general_A"] = dict(
-            workload="mamba130m_bf16 with a non-structured A (every decay is its own exp)",
-            kernel_ms_avg=kms,
-            tokens_channels_per_s=c["batch"] * c["L"] * c["dim"] / (kms * 1e-3),
-            achieved_GBps=main_res["algorithmic_bytes"] / (kms * 1e-3) / 1e9)
-        del probs, outs
-        torch.cuda.empty_cache()
+        secondary["mamba130m_bf16_general_A"] = general_A_case("mamba130m_bf16", max(10, a.steps // 2),
+                                                               5, torch, ops, W)
         secondary["varlen_mamba130m_bf16"] = varlen_case("varlen_mamba130m_bf16", max(10, a.steps // 2),
                                                          5, torch, ops, W)
         secondary["decode_fp32"] = decode_case(max(20, a.steps), 5, torch, ops, W)
@@ -521,19 +569,8 @@ def main():
         for name in W.SSD_CONFIGS:
             secondary[name] = ssd_case(name, max(10, a.steps // 2), 3, torch, ops, W)
 
-    kern_ms = main_res["kernel_ms_avg"]
-    achieved = main_res["algorithmic_bytes"] / (kern_ms * 1e-3) / 1e9
     c = W.CONFIGS[WORKLOAD]
-    elems = c["batch"] * c["L"] * c["dim"] * c["dstate"]
-    flops = FLOPS_PER_STATE_ELEMENT * elems + FLOPS_PER_TOKEN_CHANNEL * c["batch"] * c["L"] * c["dim"]
-    tflops = flops / (kern_ms * 1e-3) / 1e12
-    roof = dict(bound="alu", achieved=round(tflops, 2), peak=VALU_PEAK_TFLOPS, unit="TFLOP/s",
-                frac=round(tflops / VALU_PEAK_TFLOPS, 4), traffic=traffic_entry(kern_ms),
-                kernel="ssm_scan_fwd call = fwd_agg_kernel + fwd_carry_kernel + fwd_scan_kernel",
-                algorithmic_flops_per_launch=flops,
-                algorithmic_bytes_per_launch=main_res["algorithmic_bytes"],
-                hbm_GBps=round(achieved, 1), hbm_frac_of_peak=round(achieved / HBM_PEAK_GBPS, 4),
-                kernel_ms_avg=round(kern_ms, 5))
+    roof = main_res["roofline"]
     line = {
         "metric": METRIC,
         "value": main_res["tokens_channels_per_s"],
@@ -547,11 +584,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "batch": main_res["batch"], "seq_len": main_res["seq_len"],
-                   "dim": main_res["dim"], "dstate": main_res["dstate"], "gate": True,
-                   "A": "s4d_real (A[d,n] = -(n+1))", "input_replicas": main_res["input_replicas"]},
-        "achieved_GBps": round(achieved, 1),
-        "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
+        "config": {"workload": WORKLOAD, "batch": c["batch"], "seq_len": c["L"], "dim": c["dim"],
+                   "dstate": c["dstate"], "gate": c["gate"], "dt_range": list(c["dt_range"]),
+                   "A": "s4d_real (A[d,n] = -(n+1))",
+                   "input_replicas": main_res["input_replicas"]},
+        "achieved_GBps": roof["achieved"],
+        "pct_of_hbm_peak": round(100 * roof["frac"], 2),
         "roofline": roof,
     }
     if not a.no_cpu_baseline:

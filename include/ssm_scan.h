@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 6
+#define SSM_SCAN_ABI_VERSION 7
 
 typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
 
@@ -100,6 +100,33 @@ int ssm_scan_fwd(const void* x, const void* delta, const float* delta_bias, int 
  * (0 when none is needed).  Never fails; returns 0 for invalid sizes. */
 size_t ssm_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                                     int dtype);
+
+/*
+ * ssm_scan_fwd with the time split chosen by the caller.  The sequence is
+ * cut into chunks of chunk_len tokens (rounded up to a multiple of 8) that
+ * run in parallel and are chained through the associative composition of
+ * the per-token affine maps h -> a h + b (the local transforms that the
+ * chenyuan1125.github.io page on Mamba's selective state spaces, section
+ * "Selectivity Removes the Convolution Shortcut; Scan Restores
+ * Parallelism", combines into intervals); chunk_len >= seqlen runs every
+ * sequence as one chunk (no workspace).  chunk_len == 0 is the library's
+ * own choice, i.e. ssm_scan_fwd.  At most 65535 chunks per sequence
+ * (SSM_ERR_SHAPE beyond; chunk_len < 0 is SSM_ERR_SHAPE too).  Arguments
+ * and results as ssm_scan_fwd: any split gives the same values up to
+ * float32 rounding order.  For tuning the split on other devices and
+ * shapes, and for checking that results do not depend on it.
+ */
+int ssm_scan_fwd_chunked(const void* x, const void* delta, const float* delta_bias,
+                         int delta_softplus, const float* A, const void* B, const void* C,
+                         const float* D_skip, const void* z, void* out, float* last_state,
+                         const float* initial_state, int64_t batch, int64_t seqlen, int64_t dim,
+                         int64_t dstate, int dtype, int64_t chunk_len, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace size ssm_scan_fwd_chunked needs (0 when none is needed, or for
+ * invalid sizes). */
+size_t ssm_scan_fwd_chunked_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim,
+                                            int64_t dstate, int dtype, int64_t chunk_len);
 
 /*
  * Forward selective scan over packed variable-length sequences.

@@ -465,6 +465,20 @@ Plan plan_fwd(int64_t batch, int64_t L, int64_t dim) {
   return p;
 }
 
+// Plan with the chunk length chosen by the caller: chunk_len rounded up to
+// whole pairs of token groups; one chunk (no workspace) when it covers the
+// sequence.  K above kMaxChunks is refused by the caller.
+constexpr int64_t kMaxChunks = 65535;  // chunks per sequence: one grid dimension
+Plan plan_fwd_chunked(int64_t L, int64_t chunk_len) {
+  Plan p{1, static_cast<int>(L > 0 ? L : 1)};
+  const int64_t Lc = (chunk_len + 2 * kGroup - 1) / (2 * kGroup) * (2 * kGroup);
+  if (L <= 0 || Lc >= L) return p;
+  const int64_t K = (L + Lc - 1) / Lc;
+  p.K = static_cast<int>(K < kMaxChunks + 1 ? K : kMaxChunks + 1);
+  p.Lc = static_cast<int>(Lc);
+  return p;
+}
+
 // Workspace: ws_S (batch, K-1, dim), then ws_H (batch, K, N, dim), then ws_F
 // (K-1 ints, packed sequences only), each part 256-byte aligned.
 struct WsLayout {
@@ -540,8 +554,8 @@ int fwd_impl(const char* fn, const void* x, const void* delta, const float* delt
              int delta_softplus, const float* A, const void* B, const void* C,
              const float* D_skip, const void* z, void* out, float* last_state,
              const float* initial_state, const int* cu, int64_t nseq, int64_t batch,
-             int64_t seqlen, int64_t dim, int64_t dstate, int dtype, void* workspace,
-             size_t workspace_bytes, hipStream_t stream) {
+             int64_t seqlen, int64_t dim, int64_t dstate, int dtype, int64_t chunk_len,
+             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const bool varlen = cu != nullptr;
   if (dtype != SSM_DTYPE_F32 && dtype != SSM_DTYPE_BF16)
     return fail(SSM_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
@@ -590,7 +604,12 @@ int fwd_impl(const char* fn, const void* x, const void* delta, const float* delt
         return fail(SSM_ERR_ALIAS, "%s: output %s overlaps input %s", fn, o.name, i.name);
     }
   if (overlap(outs[0], outs[1])) return fail(SSM_ERR_ALIAS, "%s: out overlaps last_state", fn);
-  const Plan plan = plan_fwd(batch, seqlen, dim);
+  if (chunk_len < 0)
+    return fail(SSM_ERR_SHAPE, "%s: chunk_len must be >= 0, got %lld", fn, (long long)chunk_len);
+  const Plan plan = chunk_len > 0 ? plan_fwd_chunked(seqlen, chunk_len) : plan_fwd(batch, seqlen, dim);
+  if (plan.K > kMaxChunks)
+    return fail(SSM_ERR_SHAPE, "%s: chunk_len %lld cuts seqlen %lld into more than %lld chunks", fn,
+                (long long)chunk_len, (long long)seqlen, (long long)kMaxChunks);
   const WsLayout wl = workspace_layout(batch, dim, dstate, plan, varlen);
   if (workspace_bytes < wl.total || (wl.total > 0 && !workspace))
     return fail(SSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, wl.total,
@@ -661,8 +680,32 @@ int ssm_scan_fwd(const void* x, const void* delta, const float* delta_bias, int 
                  size_t workspace_bytes, hipStream_t stream) {
   g_err[0] = '\0';
   return fwd_impl("ssm_scan_fwd", x, delta, delta_bias, delta_softplus, A, B, C, D_skip, z, out,
-                  last_state, initial_state, nullptr, 0, batch, seqlen, dim, dstate, dtype,
+                  last_state, initial_state, nullptr, 0, batch, seqlen, dim, dstate, dtype, 0,
                   workspace, workspace_bytes, stream);
+}
+
+size_t ssm_scan_fwd_chunked_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim,
+                                            int64_t dstate, int dtype, int64_t chunk_len) {
+  if (chunk_len < 0) return 0;
+  if (chunk_len == 0) return ssm_scan_fwd_workspace_bytes(batch, seqlen, dim, dstate, dtype);
+  if (batch < 1 || dim < 1 || seqlen < 0 || dstate < 1 || dstate > 64 || dim > kMaxDim ||
+      batch > 65535 || seqlen > kMaxLen)
+    return 0;
+  const Plan p = plan_fwd_chunked(seqlen, chunk_len);
+  if (p.K > kMaxChunks) return 0;
+  return workspace_layout(batch, dim, dstate, p, false).total;
+}
+
+int ssm_scan_fwd_chunked(const void* x, const void* delta, const float* delta_bias,
+                         int delta_softplus, const float* A, const void* B, const void* C,
+                         const float* D_skip, const void* z, void* out, float* last_state,
+                         const float* initial_state, int64_t batch, int64_t seqlen, int64_t dim,
+                         int64_t dstate, int dtype, int64_t chunk_len, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = '\0';
+  return fwd_impl("ssm_scan_fwd_chunked", x, delta, delta_bias, delta_softplus, A, B, C, D_skip,
+                  z, out, last_state, initial_state, nullptr, 0, batch, seqlen, dim, dstate, dtype,
+                  chunk_len, workspace, workspace_bytes, stream);
 }
 
 int ssm_scan_fwd_varlen(const void* x, const void* delta, const float* delta_bias,
@@ -675,7 +718,7 @@ int ssm_scan_fwd_varlen(const void* x, const void* delta, const float* delta_bia
   if (!cu_seqlens) return fail(SSM_ERR_NULL, "ssm_scan_fwd_varlen: cu_seqlens is required");
   return fwd_impl("ssm_scan_fwd_varlen", x, delta, delta_bias, delta_softplus, A, B, C, D_skip, z,
                   out, last_state, initial_state, cu_seqlens, nseq, 1, total_len, dim, dstate,
-                  dtype, workspace, workspace_bytes, stream);
+                  dtype, 0, workspace, workspace_bytes, stream);
 }
 
 int ssm_state_update(float* state, const void* x, const void* delta, const float* delta_bias,

@@ -20,7 +20,8 @@ _DTYPES = {torch.float32: SSM_DTYPE_F32, torch.bfloat16: SSM_DTYPE_BF16}
 STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL", -2: "SSM_ERR_SHAPE", -3: "SSM_ERR_UNSUPPORTED",
           -4: "SSM_ERR_ALIGN", -5: "SSM_ERR_ALIAS", -6: "SSM_ERR_WORKSPACE", -7: "SSM_ERR_HIP"}
 
-EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd_varlen",
+EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd_chunked",
+           "ssm_scan_fwd_chunked_workspace_bytes", "ssm_scan_fwd_varlen",
            "ssm_scan_fwd_varlen_workspace_bytes", "ssm_state_update", "ssm_causal_conv1d_fwd",
            "ssm_causal_conv1d_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes",
            "ssm_ssd_fwd", "ssm_ssd_fwd_workspace_bytes", "ssm_last_error", "ssm_abi_version")
@@ -49,6 +50,11 @@ def load_library(path=LIB_PATH):
     lib.ssm_scan_fwd.restype = I
     lib.ssm_scan_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.ssm_scan_fwd_workspace_bytes.restype = SZ
+    lib.ssm_scan_fwd_chunked.argtypes = [P, P, P, I, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I,
+                                         I64, P, SZ, P]
+    lib.ssm_scan_fwd_chunked.restype = I
+    lib.ssm_scan_fwd_chunked_workspace_bytes.argtypes = [I64, I64, I64, I64, I, I64]
+    lib.ssm_scan_fwd_chunked_workspace_bytes.restype = SZ
     lib.ssm_scan_fwd_varlen.argtypes = [P, P, P, I, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64,
                                         I, P, SZ, P]
     lib.ssm_scan_fwd_varlen.restype = I
@@ -124,6 +130,27 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
     Returns ``out`` (same dtype as x), or ``(out, last_state)`` when
     ``return_last_state`` is set (or a ``last_state`` buffer is passed).
     """
+    return _scan_fwd(x, delta, A, B, C, D, z, delta_bias, delta_softplus, initial_state,
+                     return_last_state, out, last_state, workspace, stream, 0)
+
+
+def ssm_scan_fwd_chunked_workspace_bytes(batch, seqlen, dim, dstate, chunk_len,
+                                         dtype=torch.bfloat16):
+    return int(load_library().ssm_scan_fwd_chunked_workspace_bytes(batch, seqlen, dim, dstate,
+                                                                   _DTYPES[dtype], chunk_len))
+
+
+def ssm_scan_fwd_chunked(x, delta, A, B, C, chunk_len, D=None, z=None, delta_bias=None,
+                         delta_softplus=True, initial_state=None, return_last_state=False,
+                         out=None, last_state=None, workspace=None, stream=None):
+    """``ssm_scan_fwd`` with the sequence cut into chunks of ``chunk_len``
+    tokens (0 = the library's choice; >= seqlen = one chunk)."""
+    return _scan_fwd(x, delta, A, B, C, D, z, delta_bias, delta_softplus, initial_state,
+                     return_last_state, out, last_state, workspace, stream, int(chunk_len))
+
+
+def _scan_fwd(x, delta, A, B, C, D, z, delta_bias, delta_softplus, initial_state,
+              return_last_state, out, last_state, workspace, stream, chunk_len):
     lib = load_library()
     if x.dim() != 3:
         raise ValueError("x must be (batch, seqlen, dim)")
@@ -149,16 +176,17 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
     if last_state is None and return_last_state:
         last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _check(last_state, "last_state", (batch, dim, N), torch.float32, dev, optional=True)
-    need = int(lib.ssm_scan_fwd_workspace_bytes(batch, L, dim, N, _DTYPES[dt]))
+    need = int(lib.ssm_scan_fwd_chunked_workspace_bytes(batch, L, dim, N, _DTYPES[dt], chunk_len))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib.ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(A),
-                          _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(out), _ptr(last_state),
-                          _ptr(initial_state), batch, L, dim, N, _DTYPES[dt], _ptr(workspace),
-                          ws_bytes, ctypes.c_void_p(stream))
+    rc = lib.ssm_scan_fwd_chunked(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                                  _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(out),
+                                  _ptr(last_state), _ptr(initial_state), batch, L, dim, N,
+                                  _DTYPES[dt], chunk_len, _ptr(workspace), ws_bytes,
+                                  ctypes.c_void_p(stream))
     if rc != 0:
         _raise(rc)
     if last_state is not None:

@@ -25,7 +25,8 @@ def lib():
 
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
-        ["ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd_varlen",
+        ["ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd_chunked",
+         "ssm_scan_fwd_chunked_workspace_bytes", "ssm_scan_fwd_varlen",
          "ssm_scan_fwd_varlen_workspace_bytes", "ssm_state_update", "ssm_causal_conv1d_fwd",
          "ssm_causal_conv1d_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes",
          "ssm_ssd_fwd", "ssm_ssd_fwd_workspace_bytes", "ssm_last_error", "ssm_abi_version"])
@@ -47,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ssm_abi_version() == 6
+    assert lib.ssm_abi_version() == 7
 
 
 def test_workspace_query_is_host_only(lib):
@@ -59,6 +60,35 @@ def test_workspace_query_is_host_only(lib):
     # packed sequences need the per-chunk flags on top of the dense layout
     assert (lib.ssm_scan_fwd_varlen_workspace_bytes(3, 8192, 1536, 16, 1)
             > lib.ssm_scan_fwd_workspace_bytes(1, 8192, 1536, 16, 1))
+
+
+def test_chunked_workspace_query(lib):
+    f = lib.ssm_scan_fwd_chunked_workspace_bytes
+    # 0 = the library's own plan
+    assert f(4, 2048, 1536, 16, 1, 0) == lib.ssm_scan_fwd_workspace_bytes(4, 2048, 1536, 16, 1)
+    # one chunk per sequence needs no workspace
+    assert f(4, 2048, 1536, 16, 1, 2048) == 0
+    assert f(4, 2048, 1536, 16, 1, 1 << 20) == 0
+    # shorter chunks need more summaries
+    assert f(1, 4096, 64, 16, 1, 8) > f(1, 4096, 64, 16, 1, 64) > 0
+    # invalid sizes, or more than 65535 chunks per sequence
+    assert f(1, 4096, 64, 16, 1, -1) == 0
+    assert f(0, 4096, 64, 16, 1, 64) == 0
+    assert f(1, 65536 * 8 + 8, 64, 16, 1, 8) == 0
+
+
+def test_chunked_rejects_bad_chunk_len(lib):
+    P = ctypes.c_void_p
+    f = lambda k: P(0x1000000000 * k)  # far apart: no overlap at these sizes
+    call = lambda L, cl: lib.ssm_scan_fwd_chunked(f(1), f(2), None, 1, f(3), f(4), f(5), None, None,
+                                                  f(6), None, None, 1, L, 1, 16, 0, cl, None, 0,
+                                                  None)
+    assert call(64, -8) == -2
+    assert b"chunk_len" in lib.ssm_last_error()
+    assert call(65536 * 8 + 8, 8) == -2
+    assert b"chunks" in lib.ssm_last_error()
+    # a split that needs a workspace, none given
+    assert call(4096, 64) == -6
 
 
 def _fwd(lib, **kw):

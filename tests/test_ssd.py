@@ -3,19 +3,30 @@ oracle.
 
 The kernel computes the duality's matrix side on the matrix cores (bf16
 operands, float32 accumulation and state); the oracle is the recurrence.
-Outputs are bf16; the comparison is |gpu - ref| <= rtol |ref| + atol
-max|ref| with the bf16 tolerances (rtol 2e-2, atol 1e-2 relative to the
-largest magnitude: the bf16 operands of the products are rounded to 2^-9
-relative, and the sums over up to 128 states and 64 tokens scale with the
-output's range).  Cases cover one and many chunks, ragged last chunks,
-both state widths, several groups, every optional input, resume in place,
-and the Mamba-2-2.7B-shaped layer on sampled heads.
+Each element is held to its own bound, derived from the operands the
+kernel rounds to bf16 (unit roundoff u = 2^-8; see tests/_ssd_bound.py):
+    |gpu - ref| <= 2u |ref| + 2u (E1 + E2) |silu(z)| + 1e-6
+for the bf16 outputs (the first term covers their own rounding, the second
+the rounded scores, decay-weighted inputs and state copies, E1 and E2
+being sums of the magnitudes of exactly the terms those roundings touch),
+and
+    |gpu - ref| <= 2u S_last + 2^-20 |ref| + 1e-6
+for the float32 final state (S_last: the magnitudes of the rounded
+decay-weighted inputs that reach it).  The factor 2 is margin over the
+first-order bound (a bf16-rounding emulation of the kernel stays below
+0.95 of it).  The bound exceeds |ref| only where the terms cancel (about
+1-3% of the elements); the tests assert that such elements stay below 5%,
+so that nearly every element can fail.
+Cases cover one and many chunks, ragged last chunks, both state widths,
+several groups, every optional input, resume in place, and the
+Mamba-2-2.7B-shaped layer on sampled heads.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
+from tests._ssd_bound import silu, ssd_budget
 from selective_state_space_31_amd import ssm_ssd_fwd
 from selective_state_space_31_amd.workloads import SSD_CONFIGS, make_ssd_problem
 
@@ -27,16 +38,25 @@ def host(t):
     return None if t is None else t.to(torch.float32).cpu().numpy()
 
 
-def close(got, ref, what, rtol=2e-2, atol=1e-2):
+U = 2.0 ** -8  # unit roundoff of bf16 (8 significant bits, round to nearest even)
+
+
+def check(got, ref, budget, what, rel=2 * U, slack=1e-6):
+    """|got - ref| <= rel |ref| + 2 budget + slack elementwise, and the bound
+    must stay below |ref| on all but a few elements."""
     got = np.asarray(got, np.float64)
-    at = atol * max(1.0, float(np.max(np.abs(ref)))) if ref.size else atol
-    err = np.abs(got - ref)
-    bad = err > at + rtol * np.abs(ref)
     assert np.isfinite(got).all(), what + ": non-finite"
+    tol = rel * np.abs(ref) + 2.0 * budget + slack
+    err = np.abs(got - ref)
+    bad = err > tol
     if bad.any():
-        i = np.unravel_index(np.argmax(err - at - rtol * np.abs(ref)), err.shape)
-        raise AssertionError("%s: %d of %d outside; worst at %s got %r ref %r (atol %g)"
-                             % (what, int(bad.sum()), bad.size, i, got[i], ref[i], at))
+        i = np.unravel_index(np.argmax(err / tol), err.shape)
+        raise AssertionError("%s: %d of %d outside; worst at %s got %r ref %r (bound %g)"
+                             % (what, int(bad.sum()), bad.size, i, got[i], ref[i], tol[i]))
+    if ref.size >= 256:
+        vac = float(np.mean(tol >= np.abs(ref)))
+        assert vac < 0.05, "%s: the bound exceeds |ref| on %.1f%% of the elements" % (what, 100 * vac)
+    return float(np.max(err / tol)) if err.size else 0.0
 
 
 def run_and_compare(p, what, heads=None):
@@ -44,20 +64,34 @@ def run_and_compare(p, what, heads=None):
     out, last = ssm_ssd_fwd(p.x, p.dt, p.A, p.B, p.C, D=p.D, z=p.z, dt_bias=p.dt_bias,
                             dt_softplus=p.dt_softplus, initial_state=p.h0, return_last_state=True)
     torch.cuda.synchronize()
-    hs = slice(None) if heads is None else heads
     sub = lambda t, ax: None if t is None else (t if heads is None else t.index_select(ax, heads))
-    G = p.G
     if heads is not None:
-        assert G == 1
-    ref, ref_last = oracle.ssd_scan(host(sub(p.x, 2)), host(sub(p.dt, 2)), host(sub(p.A, 0)),
-                                    host(p.B), host(p.C), D=host(sub(p.D, 0)), z=host(sub(p.z, 2)),
-                                    dt_bias=host(sub(p.dt_bias, 0)), dt_softplus=p.dt_softplus,
-                                    h0=host(sub(p.h0, 1)))
+        assert p.G == 1
+    ins = dict(x=host(sub(p.x, 2)), dt=host(sub(p.dt, 2)), A=host(sub(p.A, 0)), B=host(p.B),
+               C=host(p.C), dt_bias=host(sub(p.dt_bias, 0)), h0=host(sub(p.h0, 1)))
+    z = host(sub(p.z, 2))
+    ref, ref_last = oracle.ssd_scan(ins["x"], ins["dt"], ins["A"], ins["B"], ins["C"],
+                                    D=host(sub(p.D, 0)), z=z, dt_bias=ins["dt_bias"],
+                                    dt_softplus=p.dt_softplus, h0=ins["h0"])
+    E1, E2, S_last = ssd_budget(ins["x"], ins["dt"], ins["A"], ins["B"], ins["C"],
+                                dt_bias=ins["dt_bias"], dt_softplus=p.dt_softplus, h0=ins["h0"])
+    E = E1 + E2
+    gate = 1.0 if z is None else np.abs(silu(z))
     got = out if heads is None else out.index_select(2, heads)
     gl = last if heads is None else last.index_select(1, heads)
-    close(host(got), ref, what + " out")
-    close(host(gl), ref_last, what + " last_state")
+    r1 = check(host(got), ref, U * E * gate, what + " out")
+    r2 = check(host(gl), ref_last, U * S_last, what + " last_state", rel=2.0 ** -20)
+    print("  worst |err| / bound: out %.3f, last_state %.3f" % (r1, r2), flush=True)
     return out, last
+
+
+def full_budget(p, h0):
+    """Budgets (u E |silu(z)|, u S_last) of a whole problem with initial state h0."""
+    E1, E2, S_last = ssd_budget(host(p.x), host(p.dt), host(p.A), host(p.B), host(p.C),
+                                dt_bias=host(p.dt_bias), dt_softplus=p.dt_softplus, h0=h0)
+    E = E1 + E2
+    gate = 1.0 if p.z is None else np.abs(silu(host(p.z)))
+    return U * E * gate, U * S_last
 
 
 SHAPES = [  # (batch, L, H, N, G)
@@ -103,8 +137,9 @@ def test_resume_in_place_and_split():
     torch.cuda.synchronize()
     ref, ref_last = oracle.ssd_scan(host(p.x), host(p.dt), host(p.A), host(p.B), host(p.C),
                                     D=host(p.D), z=host(p.z), dt_bias=host(p.dt_bias), h0=host(p.h0))
-    close(host(torch.cat(parts, 1)), ref, "split out")
-    close(host(st), ref_last, "split last_state")
+    Eg, Sl = full_budget(p, host(p.h0))
+    check(host(torch.cat(parts, 1)), ref, Eg, "split out")
+    check(host(st), ref_last, Sl, "split last_state", rel=2.0 ** -20)
 
 
 def test_resume_in_place_over_segments():
@@ -119,8 +154,9 @@ def test_resume_in_place_over_segments():
     torch.cuda.synchronize()
     ref, ref_last = oracle.ssd_scan(host(p.x), host(p.dt), host(p.A), host(p.B), host(p.C),
                                     D=host(p.D), z=host(p.z), dt_bias=host(p.dt_bias), h0=host(h0))
-    close(host(out), ref, "in place out")
-    close(host(st), ref_last, "in place last_state")
+    Eg, Sl = full_budget(p, host(h0))
+    check(host(out), ref, Eg, "in place out")
+    check(host(st), ref_last, Sl, "in place last_state", rel=2.0 ** -20)
 
 
 def test_config_ssd_mamba2_2p7b_bf16_sampled_heads():
