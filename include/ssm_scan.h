@@ -129,6 +129,28 @@ size_t ssm_scan_fwd_chunked_workspace_bytes(int64_t batch, int64_t seqlen, int64
                                             int64_t dstate, int dtype, int64_t chunk_len);
 
 /*
+ * ssm_scan_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments and results as ssm_scan_fwd, without the workspace: the chunk
+ * summaries go to a scratch array that the library holds on each device it
+ * runs on (64 MiB, reserved with the library's code on that device until
+ * the process ends; its device address is looked up once per device, on
+ * the first call made with that device current).  This call allocates
+ * nothing.  Sizes whose ssm_scan_fwd_workspace_bytes exceeds 64 MiB are
+ * refused with SSM_ERR_WORKSPACE (use ssm_scan_fwd with a workspace).
+ * Every call on one device shares that device's scratch, which keeps the
+ * last call's contents (nothing in it needs to start at zero): calls that
+ * overlap in time on one device -- on different streams, or from different
+ * host threads without ordering -- race and give wrong results.  Calls
+ * ordered on one stream are fine.
+ */
+int ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* delta_bias,
+                         int delta_softplus, const float* A, const void* B, const void* C,
+                         const float* D_skip, const void* z, void* out, float* last_state,
+                         const float* initial_state, int64_t batch, int64_t seqlen, int64_t dim,
+                         int64_t dstate, int dtype, hipStream_t stream);
+
+/*
  * Forward selective scan over packed variable-length sequences.
  * Padding a batch of unequal sequences on the right feeds the padding tokens
  * through the recurrence and changes the state they leave behind; the

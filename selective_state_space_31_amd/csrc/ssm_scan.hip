@@ -26,6 +26,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "ssm_scan.h"
 
@@ -645,6 +646,49 @@ int fwd_impl(const char* fn, const void* x, const void* delta, const float* delt
   return dispatch_fwd(a, batch, delta_softplus != 0, stream);
 }
 
+// ----------------------------------------------------------------------------
+// library-held scratch for ssm_scan_fwd_noalloc
+//
+// The forward's chunk summaries live in a file-scope device array instead of
+// a caller-provided workspace, for callers that cannot allocate.  Each
+// device that runs the call holds its own copy (allocated with the code
+// object, kept until the process ends).  In host code `scratch` names a
+// host-side stand-in, never the device memory: the device address is taken
+// once per device with hipGetSymbolAddress and only that address is passed
+// to kernels.
+// ----------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t{64} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device), or nullptr with the status in *rc.
+void* scratch_on_current_device(int* rc) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *rc = fail(SSM_ERR_HIP, "ssm_scan_fwd_noalloc: no usable current device (%s)",
+               e != hipSuccess ? hipGetErrorString(e) : "device index out of range");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *rc = fail(SSM_ERR_HIP, "ssm_scan_fwd_noalloc: hipGetSymbolAddress(scratch) failed: %s",
+                 hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *rc = SSM_OK;
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace ssm
 
 using namespace ssm;
@@ -682,6 +726,28 @@ int ssm_scan_fwd(const void* x, const void* delta, const float* delta_bias, int 
   return fwd_impl("ssm_scan_fwd", x, delta, delta_bias, delta_softplus, A, B, C, D_skip, z, out,
                   last_state, initial_state, nullptr, 0, batch, seqlen, dim, dstate, dtype, 0,
                   workspace, workspace_bytes, stream);
+}
+
+int ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* delta_bias,
+                         int delta_softplus, const float* A, const void* B, const void* C,
+                         const float* D_skip, const void* z, void* out, float* last_state,
+                         const float* initial_state, int64_t batch, int64_t seqlen, int64_t dim,
+                         int64_t dstate, int dtype, hipStream_t stream) {
+  g_err[0] = '\0';
+  const size_t need = ssm_scan_fwd_workspace_bytes(batch, seqlen, dim, dstate, dtype);
+  if (need > kScratchBytes)
+    return fail(SSM_ERR_WORKSPACE,
+                "ssm_scan_fwd_noalloc: these sizes need %zu bytes of scratch, the library holds %zu "
+                "(use ssm_scan_fwd with a workspace)", need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    int rc = SSM_OK;
+    ws = scratch_on_current_device(&rc);
+    if (!ws) return rc;
+  }
+  return fwd_impl("ssm_scan_fwd_noalloc", x, delta, delta_bias, delta_softplus, A, B, C, D_skip,
+                  z, out, last_state, initial_state, nullptr, 0, batch, seqlen, dim, dstate, dtype,
+                  0, ws, ws ? kScratchBytes : 0, stream);
 }
 
 size_t ssm_scan_fwd_chunked_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim,

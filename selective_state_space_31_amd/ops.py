@@ -21,7 +21,7 @@ STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL", -2: "SSM_ERR_SHAPE", -3: "SSM_ERR_UNS
           -4: "SSM_ERR_ALIGN", -5: "SSM_ERR_ALIAS", -6: "SSM_ERR_WORKSPACE", -7: "SSM_ERR_HIP"}
 
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd_chunked",
-           "ssm_scan_fwd_chunked_workspace_bytes", "ssm_scan_fwd_varlen",
+           "ssm_scan_fwd_chunked_workspace_bytes", "ssm_scan_fwd_noalloc", "ssm_scan_fwd_varlen",
            "ssm_scan_fwd_varlen_workspace_bytes", "ssm_state_update", "ssm_causal_conv1d_fwd",
            "ssm_causal_conv1d_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes",
            "ssm_ssd_fwd", "ssm_ssd_fwd_workspace_bytes", "ssm_last_error", "ssm_abi_version")
@@ -55,6 +55,8 @@ def load_library(path=LIB_PATH):
     lib.ssm_scan_fwd_chunked.restype = I
     lib.ssm_scan_fwd_chunked_workspace_bytes.argtypes = [I64, I64, I64, I64, I, I64]
     lib.ssm_scan_fwd_chunked_workspace_bytes.restype = SZ
+    lib.ssm_scan_fwd_noalloc.argtypes = [P, P, P, I, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I, P]
+    lib.ssm_scan_fwd_noalloc.restype = I
     lib.ssm_scan_fwd_varlen.argtypes = [P, P, P, I, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64,
                                         I, P, SZ, P]
     lib.ssm_scan_fwd_varlen.restype = I
@@ -147,6 +149,46 @@ def ssm_scan_fwd_chunked(x, delta, A, B, C, chunk_len, D=None, z=None, delta_bia
     tokens (0 = the library's choice; >= seqlen = one chunk)."""
     return _scan_fwd(x, delta, A, B, C, D, z, delta_bias, delta_softplus, initial_state,
                      return_last_state, out, last_state, workspace, stream, int(chunk_len))
+
+
+def ssm_scan_fwd_noalloc(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                         initial_state=None, out=None, last_state=None, stream=None):
+    """``ssm_scan_fwd`` with the library's own device scratch instead of a
+    workspace (the C call allocates nothing; ``out`` and ``last_state`` are
+    allocated here only when not passed).  Calls overlapping in time on one
+    device race on that scratch."""
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, seqlen, dim)")
+    batch, L, dim = x.shape
+    N = A.shape[1]
+    dev, dt = x.device, x.dtype
+    if dt not in _DTYPES:
+        raise TypeError("activations must be float32 or bfloat16, got %s" % dt)
+    _check(x, "x", (batch, L, dim), dt, dev)
+    _check(delta, "delta", (batch, L, dim), dt, dev)
+    _check(z, "z", (batch, L, dim), dt, dev, optional=True)
+    _check(B, "B", (batch, L, N), dt, dev)
+    _check(C, "C", (batch, L, N), dt, dev)
+    _check(A, "A", (dim, N), torch.float32, dev)
+    _check(D, "D", (dim,), torch.float32, dev, optional=True)
+    _check(delta_bias, "delta_bias", (dim,), torch.float32, dev, optional=True)
+    _check(initial_state, "initial_state", (batch, dim, N), torch.float32, dev, optional=True)
+    if out is None:
+        out = torch.empty((batch, L, dim), dtype=dt, device=dev)
+    _check(out, "out", (batch, L, dim), dt, dev)
+    _check(last_state, "last_state", (batch, dim, N), torch.float32, dev, optional=True)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssm_scan_fwd_noalloc(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                                  _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(out),
+                                  _ptr(last_state), _ptr(initial_state), batch, L, dim, N,
+                                  _DTYPES[dt], ctypes.c_void_p(stream))
+    if rc != 0:
+        _raise(rc)
+    if last_state is not None:
+        return out, last_state
+    return out
 
 
 def _scan_fwd(x, delta, A, B, C, D, z, delta_bias, delta_softplus, initial_state,

@@ -26,7 +26,7 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd_chunked",
-         "ssm_scan_fwd_chunked_workspace_bytes", "ssm_scan_fwd_varlen",
+         "ssm_scan_fwd_chunked_workspace_bytes", "ssm_scan_fwd_noalloc", "ssm_scan_fwd_varlen",
          "ssm_scan_fwd_varlen_workspace_bytes", "ssm_state_update", "ssm_causal_conv1d_fwd",
          "ssm_causal_conv1d_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes",
          "ssm_ssd_fwd", "ssm_ssd_fwd_workspace_bytes", "ssm_last_error", "ssm_abi_version"])
@@ -89,6 +89,20 @@ def test_chunked_rejects_bad_chunk_len(lib):
     assert b"chunks" in lib.ssm_last_error()
     # a split that needs a workspace, none given
     assert call(4096, 64) == -6
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """Sizes whose workspace exceeds the 64 MiB scratch are refused on the
+    host, before the scratch is looked up or anything is enqueued."""
+    P = ctypes.c_void_p
+    f = lambda k: P(0x10000000000 * k)
+    # batch 1, 1024 channels, 2^20 tokens: chunk summaries of well over 64 MiB
+    need = lib.ssm_scan_fwd_workspace_bytes(1, 1 << 20, 1024, 64, 0)
+    assert need > 64 << 20
+    rc = lib.ssm_scan_fwd_noalloc(f(1), f(2), None, 1, f(3), f(4), f(5), None, None, f(6), None,
+                                  None, 1, 1 << 20, 1024, 64, 0, None)
+    assert rc == -6
+    assert b"scratch" in lib.ssm_last_error()
 
 
 def _fwd(lib, **kw):
