@@ -110,20 +110,17 @@ __device__ __forceinline__ void load_row(const bf16_t* p, int N, float (&v)[NT])
 // ----------------------------------------------------------------------------
 // scalar functions of the step
 // ----------------------------------------------------------------------------
-// softplus(u) = log(1 + e^u) in float32, accurate to a few ulp relative:
-//   u > 15      : u (the dropped log1p(e^-u) < 3.1e-7 is below u's half-ulp)
-//   e^u < 1/16  : log1p(e) by its series to e^5 (relative error < e^5/6)
-//   otherwise   : log2(1 + e) * ln 2 (1 + e >= 1.0625 keeps cancellation small)
+// softplus(u) = log(1 + e^u) = max(u, 0) + log1p(e) with e = e^-|u| in (0, 1],
+// in float32.  log1p(e) is log(w) for w = 1 + e rounded, plus the rounding
+// error c = e - (w - 1) (exact: w - 1 is exact and e <= 1) divided by w; c
+// itself stands in for c / w, off by at most c (1 - 1/w) < 2^-25 e.  Relative
+// error a few ulp (measured against float64 over [-40, 40]: at most 1.9e-6,
+// where the exponential's own argument rounding dominates).
 __device__ __forceinline__ float softplus_f32(float u) {
-  const float e = __builtin_amdgcn_exp2f(u * kLog2e);
-  const float lg = __builtin_amdgcn_logf(1.0f + e) * kLn2;
-  const float p =
-      e * __builtin_fmaf(e, __builtin_fmaf(e, __builtin_fmaf(e, __builtin_fmaf(e, 0.2f, -0.25f),
-                                                               0.33333334f),
-                                             -0.5f),
-                         1.0f);
-  const float r = e < 0.0625f ? p : lg;
-  return u > 15.0f ? u : r;
+  const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(u) * kLog2e);
+  const float w = 1.0f + e;
+  const float c = e - (w - 1.0f);
+  return __builtin_fmaxf(u, 0.0f) + __builtin_fmaf(__builtin_amdgcn_logf(w), kLn2, c);
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z); e^-z = inf gives 0 * z = -0.
@@ -216,6 +213,14 @@ struct FwdArgs {
   int K;
   int dim;
   int N;
+  // grouped forward (fwd_sum_kernel / fwd_out_kernel): chunks go in groups of
+  // G consecutive ones, one wave each; ws_S / ws_H / ws_F then hold every
+  // chunk's exclusive prefix within its group ((batch, K, dim), (batch, K, N,
+  // dim), (batch, K)), and these the groups' aggregates
+  int G;
+  float* ws_AS;  // (batch, Kg, dim)
+  float* ws_AH;  // (batch, Kg, N, dim)
+  int* ws_AF;    // (batch, Kg)
 };
 
 constexpr int kGroup = 4;  // tokens per group; the next group's loads are in flight
@@ -246,9 +251,10 @@ struct Chan {
 };
 
 template <typename TA, int NT, bool EXACT>
-__device__ __forceinline__ Chan<NT> load_chan(const FwdArgs<TA>& a, int d0) {
+__device__ __forceinline__ Chan<NT> load_chan(const FwdArgs<TA>& a, int d0,
+                                              bool write_table = true) {
   Chan<NT> c;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int d = d0 + lane;
   const int N = a.N;
   c.d0 = d0;
@@ -269,7 +275,7 @@ __device__ __forceinline__ Chan<NT> load_chan(const FwdArgs<TA>& a, int d0) {
       v[j] = an * kLog2e;
       if (EXACT || n < N) pow_ok = pow_ok && (an == static_cast<float>(n + 1) * c.A0);
     }
-    tab[q * 64 + lane] = f32x4{v[0], v[1], v[2], v[3]};
+    if (write_table) tab[q * 64 + lane] = f32x4{v[0], v[1], v[2], v[3]};
   }
   c.pow = __all(pow_ok);
   c.bias = a.bias ? a.bias[dl] : 0.0f;
@@ -343,7 +349,7 @@ __device__ __forceinline__ void step_block(float (&h)[NT], const Chan<NT>& ch, S
     const volatile f32x4* tab = a2_table<NT>();
 #pragma unroll
     for (int q = 0; q < NB / 4; ++q) {
-      const f32x4 v = tab[(n0 / 4 + q) * 64 + threadIdx.x];
+      const f32x4 v = tab[(n0 / 4 + q) * 64 + (threadIdx.x & 63)];
       const float a2[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -662,30 +668,347 @@ __global__ void __launch_bounds__(64) fwd_agg_kernel(FwdArgs<TA> a) {
   if (VL && blockIdx.x == 0 && threadIdx.x == 0) a.ws_F[c] = reset ? 1 : 0;
 }
 
-// Output pass: block (channel tile, chunk c, sequence b).  With packed
-// sequences the chunk is walked segment by segment (the parts of it that
-// belong to one sequence): the state is reset at each sequence start and
-// stored to last_state at each sequence end.
-template <typename TA, int NT, bool EXACT, bool SP, bool GATE, bool VL>
-__global__ void __launch_bounds__(64) fwd_scan_kernel(FwdArgs<TA> a) {
+// ----------------------------------------------------------------------------
+// grouped forward: two launches
+//
+// Chunks are taken in groups of G consecutive ones, a workgroup of G waves
+// per (channel tile, group, sequence), one wave per chunk.
+//   fwd_sum_kernel : each wave summarises its chunk (as fwd_agg_kernel), the
+//                    group's waves scan their summaries in LDS (inclusive,
+//                    log2 G rounds of the composition), and leave each
+//                    chunk's exclusive prefix within the group and the
+//                    group's aggregate;
+//   fwd_out_kernel : the waves of a group compose the aggregates of the
+//                    groups before it (split over the waves, then folded in
+//                    LDS), apply their chunk's prefix and run the chunk.
+// A chunk summary is the affine map h -> (F ? 0 : e^(A S)) h + H (F: the state
+// entering the chunk is forgotten -- a packed sequence starts in it, or, in
+// the (batch, L) layout, chunk 0, whose summary starts from the initial state
+// so that the output pass never reads initial_state, which may be
+// last_state).  The maps compose as (F1,S1,H1) then (F2,S2,H2) =
+// (F1|F2, F2 ? S2 : S1+S2, F2 ? H2 : e^(A S2) H1 + H2), associatively.
+// ----------------------------------------------------------------------------
+// Largest group (waves per workgroup): 8 for the exact state widths <= 32, 4
+// for the padded widths and 64.
+constexpr int group_max(int NT, bool EXACT) { return (EXACT && NT <= 32) ? 8 : 4; }
+// Waves per SIMD the grouped kernels must allow.  A group of G waves puts G/4
+// on each SIMD, so with G = 8 the occupancy comes in steps of 2: 6 for the
+// exact widths <= 16 (80 VGPRs, and a scalar budget that keeps the walk's B/C
+// rows and buffer descriptors in SGPRs without spilling; 8 would cap the
+// SGPRs below what the walk holds), 2 for the padded widths, 1 for the wide
+// ones (their registers decide).  The host's plan assumes the same
+// occupancy (fwd_waves_per_simd).
+constexpr int group_min_waves(int NT, bool EXACT) { return NT <= 16 ? (EXACT ? 6 : 2) : 1; }
+// LDS of the group scan: per wave slot S[64], H[NT][64], F.
+template <int NT>
+constexpr size_t group_lds_bytes(int G) {
+  return static_cast<size_t>(G) * (NT + 1) * 64 * 4 + static_cast<size_t>(G) * 4;
+}
+
+// Calls f(n, exp(A[d,n] S)) for the lane's channel, n = 0 .. NT-1 (ACC: each
+// decay to ~0.5 ulp): powers of e^(A[d,0] S) when A has the S4D-real shape,
+// else one exponential per state from the exponent table.
+template <int NT, bool ACC, class Fn>
+__device__ __forceinline__ void for_decays(const Chan<NT>& ch, float S, Fn f) {
+  if (ch.pow) {
+    float rh, rl = 0.0f;
+    if constexpr (ACC) {
+      rh = exp_acc(ch.A0 * S, rl);
+    } else {
+      rh = __builtin_amdgcn_exp2f(ch.A2_0 * S);
+    }
+    float p = rh;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      f(n, p);
+      if constexpr (ACC) {
+        p = __builtin_fmaf(p, rh, p * rl);
+      } else {
+        p *= rh;
+      }
+    }
+  } else {
+    const volatile f32x4* tab = a2_table<NT>();
+#pragma unroll
+    for (int q = 0; q < NT / 4; ++q) {
+      const f32x4 v = tab[q * 64 + (threadIdx.x & 63)];
+      const float a2[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (ACC) {
+          float lo;
+          f(4 * q + k, exp_acc(a2[k] * S * kLn2, lo));
+        } else {
+          f(4 * q + k, __builtin_amdgcn_exp2f(a2[k] * S));
+        }
+      }
+    }
+  }
+}
+
+// R <- (L then R), L's state values read through lh(n).  F is wave-uniform.
+template <int NT, bool ACC, class LH>
+__device__ __forceinline__ void compose(const Chan<NT>& ch, float LS, LH lh, int LF, float& RS,
+                                        float (&RH)[NT], int& RF) {
+  if (RF) return;  // R forgets the state entering it
+  for_decays<NT, ACC>(ch, RS, [&](int n, float e) { RH[n] = __builtin_fmaf(e, lh(n), RH[n]); });
+  RS += LS;
+  RF = LF;
+}
+
+// X <- (X then R), R's state values read through rh(n).
+template <int NT, bool ACC, class RHF>
+__device__ __forceinline__ void append(const Chan<NT>& ch, float& XS, float (&XH)[NT], int& XF,
+                                       float RS, RHF rh, int RF) {
+  if (RF) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) XH[n] = rh(n);
+    XS = RS;
+    XF = 1;
+    return;
+  }
+  for_decays<NT, ACC>(ch, RS, [&](int n, float e) { XH[n] = __builtin_fmaf(e, XH[n], rh(n)); });
+  XS += RS;
+}
+
+// Slots of the group scan buffer (dynamic LDS), one per wave.
+template <int NT>
+struct GroupSlots {
+  float* S;
+  float* H;
+  int* F;
+  __device__ explicit GroupSlots(int G) {
+    extern __shared__ float dyn_lds[];
+    S = dyn_lds;
+    H = dyn_lds + G * 64;
+    F = reinterpret_cast<int*>(dyn_lds + static_cast<size_t>(G) * (NT + 1) * 64);
+  }
+  __device__ void put(int w, float s, const float (&h)[NT], int f) const {
+    const int lane = threadIdx.x & 63;
+    S[w * 64 + lane] = s;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) H[(w * NT + n) * 64 + lane] = h[n];
+    if (lane == 0) F[w] = f;
+  }
+  __device__ float s(int w) const { return S[w * 64 + (threadIdx.x & 63)]; }
+  __device__ float h(int w, int n) const { return H[(w * NT + n) * 64 + (threadIdx.x & 63)]; }
+  __device__ int f(int w) const { return __builtin_amdgcn_readfirstlane(F[w]); }
+};
+
+// One summary slot in the workspace (S at S + slot*dim, H at H + slot*N*dim,
+// channel-fastest) accessed through buffer descriptors: a scalar base at the
+// tile's first channel d0, the lane's channel as the vector offset and the
+// state's row as a scalar offset, so that N states cost no vector address
+// arithmetic.
+struct WsSlot {
+  rsrc_t s, h;
+  uint32_t row;  // bytes per state row
+  __device__ WsSlot(const float* S, const float* H, size_t slot, int N, int dim, int d0) {
+    s = make_rsrc(S + slot * dim + d0, static_cast<uint32_t>(dim - d0) * 4);
+    h = make_rsrc(H + slot * N * dim + d0, static_cast<uint32_t>(N * dim - d0) * 4);
+    row = static_cast<uint32_t>(dim) * 4;
+  }
+  // vo: the lane's byte offset from d0 (out of range: stores dropped)
+  __device__ float ld_s(uint32_t vo) const {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(s, vo, 0, 0));
+  }
+  __device__ float ld_h(int n, uint32_t vo) const {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(h, vo, n * row, 0));
+  }
+  __device__ void st_s(float v, uint32_t vo) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), s, vo, 0, 0);
+  }
+  __device__ void st_h(int n, float v, uint32_t vo) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), h, vo, n * row, 0);
+  }
+};
+
+// Summary pass: block (channel tile, group j, sequence b) of G waves; wave w
+// summarises chunk c = j G + w (c <= K-2; the others carry the identity).
+template <typename TA, int NT, bool EXACT, bool SP, bool VL>
+__global__ void __launch_bounds__(64 * group_max(NT, EXACT), group_min_waves(NT, EXACT))
+    fwd_sum_kernel(FwdArgs<TA> a) {
+  constexpr bool ACC = sizeof(TA) == 4;
+  // wave index, made wave-uniform so that everything derived from it stays scalar
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = static_cast<int>(threadIdx.x & 63);
+  const int G = a.G;
   const int d0 = blockIdx.x * 64;
-  const int c = blockIdx.y;
+  const int j = blockIdx.y;
   const int b = blockIdx.z;
-  const Chan<NT> ch = load_chan<TA, NT, EXACT>(a, d0);
+  const int c = j * G + w;
+  const Chan<NT> ch = load_chan<TA, NT, EXACT>(a, d0, w == 0);
+  __syncthreads();  // the exponent table is written
   const int N = a.N;
-  const int d = d0 + threadIdx.x;
+  const int d = d0 + lane;
   const int dl = ch.valid ? d : a.dim - 1;
-  float h[NT];
-  if (a.K > 1) {
-    // state entering the chunk, left by the carry pass (also for c = 0, so
-    // that this pass never reads initial_state, which may be last_state)
+  float H[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) H[n] = 0.0f;
+  float S = 0.0f;
+  int F = 0;
+  if (c < a.K - 1) {
+    const int t_begin = c * a.Lc;  // chunks before the last are full
+    bool reset = false;
+    if constexpr (VL) {
+      const int t_end = t_begin + a.Lc;
+      const int s = seq_owner(a.cu, a.nseq, t_end - 1);
+      const int st = a.cu[s];
+      if (st >= t_begin && st < t_end) {
+        reset = true;
+        load_h0<NT, EXACT>(a.h0, s, a.dim, dl, N, H);
+        if (ch.pow)
+          run_tokens<TA, NT, EXACT, SP, false, true, true>(a, ch, b, st, t_end - st, H, S);
+        else
+          run_tokens<TA, NT, EXACT, SP, false, false, true>(a, ch, b, st, t_end - st, H, S);
+      }
+    }
+    if (!reset) {
+      constexpr bool REV = EXACT && NT <= 16 && sizeof(TA) == 2 && (sizeof(TA) * NT) % 4 == 0;
+      if (ch.pow) {
+        if constexpr (REV)
+          agg_reverse<TA, NT, SP>(a, ch, b, t_begin, a.Lc, H, S);
+        else
+          run_tokens<TA, NT, EXACT, SP, false, true, true>(a, ch, b, t_begin, a.Lc, H, S);
+      } else {
+        run_tokens<TA, NT, EXACT, SP, false, false, true>(a, ch, b, t_begin, a.Lc, H, S);
+      }
+    }
+    F = reset ? 1 : 0;
+    if (!VL && c == 0) {
+      // the chunk's map applied to the initial state: H <- e^(A S) h0 + H
+      const float* hp = a.h0 ? a.h0 + (static_cast<size_t>(b) * a.dim + dl) * N : nullptr;
+      compose<NT, ACC>(ch, 0.0f, [&](int n) { return (hp && (EXACT || n < N)) ? hp[n] : 0.0f; },
+                       1, S, H, F);
+      F = 1;
+    }
+  }
+  // inclusive scan of the G summaries (Hillis-Steele over the waves)
+  const GroupSlots<NT> slots(G);
+  for (int o = 1; o < G; o <<= 1) {
+    slots.put(w, S, H, F);
+    __syncthreads();
+    if (w >= o)
+      compose<NT, ACC>(ch, slots.s(w - o), [&](int n) { return slots.h(w - o, n); },
+                       slots.f(w - o), S, H, F);
+    __syncthreads();
+  }
+  slots.put(w, S, H, F);
+  __syncthreads();
+  // chunk c's exclusive prefix within the group (the identity at a group's
+  // first chunk is not stored, except in the first group: there it is the
+  // initial state, or nothing for packed sequences)
+  if (c < a.K && (w > 0 || j == 0)) {
+    float es = 0.0f, eh[NT];
+    int ef = 0;
+    if (w > 0) {
+      es = slots.s(w - 1);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) eh[n] = slots.h(w - 1, n);
+      ef = slots.f(w - 1);
+    } else if constexpr (!VL) {
+      load_h0<NT, EXACT>(a.h0, b, a.dim, dl, N, eh);
+      ef = 1;
+    } else {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) eh[n] = 0.0f;
+    }
     const size_t slot = static_cast<size_t>(b) * a.K + c;
+    // lanes past the last channel store out of the descriptor's range (dropped)
+    const WsSlot ws(a.ws_S, a.ws_H, slot, N, a.dim, d0);
+    const uint32_t vo = ch.valid ? static_cast<uint32_t>(lane) * 4 : kOutOfRange;
+    ws.st_s(es, vo);
 #pragma unroll
     for (int n = 0; n < NT; ++n)
-      h[n] = (EXACT || n < N) ? a.ws_H[(slot * N + n) * a.dim + dl] : 0.0f;
-  } else {
-    load_h0<NT, EXACT>(VL ? nullptr : a.h0, b, a.dim, dl, N, h);
+      if (EXACT || n < N) ws.st_h(n, eh[n], vo);
+    if (blockIdx.x == 0 && lane == 0) a.ws_F[slot] = ef;
   }
+  // the group's aggregate, when a chunk follows the group
+  if (w == G - 1 && (j + 1) * G < a.K) {
+    const int Kg = (a.K + G - 1) / G;
+    const size_t slot = static_cast<size_t>(b) * Kg + j;
+    const WsSlot ws(a.ws_AS, a.ws_AH, slot, N, a.dim, d0);
+    const uint32_t vo = ch.valid ? static_cast<uint32_t>(lane) * 4 : kOutOfRange;
+    ws.st_s(S, vo);
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      if (EXACT || n < N) ws.st_h(n, H[n], vo);
+    if (blockIdx.x == 0 && lane == 0) a.ws_AF[slot] = F;
+  }
+}
+
+// Output pass: block (channel tile, group j, sequence b) of G waves; wave w
+// runs chunk c = j G + w from its entering state.  With packed sequences the
+// chunk is walked segment by segment (the parts of it that belong to one
+// sequence): the state is reset at each sequence start and stored to
+// last_state at each sequence end.  K == 1: one wave per block, no prologue.
+template <typename TA, int NT, bool EXACT, bool SP, bool GATE, bool VL>
+__global__ void __launch_bounds__(64 * group_max(NT, EXACT), group_min_waves(NT, EXACT))
+    fwd_out_kernel(FwdArgs<TA> a) {
+  constexpr bool ACC = sizeof(TA) == 4;
+  // wave index, made wave-uniform so that everything derived from it stays scalar
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = static_cast<int>(threadIdx.x & 63);
+  const int G = a.G;
+  const int d0 = blockIdx.x * 64;
+  const int j = blockIdx.y;
+  const int b = blockIdx.z;
+  const int c = j * G + w;
+  const Chan<NT> ch = load_chan<TA, NT, EXACT>(a, d0, w == 0);
+  __syncthreads();  // the exponent table is written
+  const int N = a.N;
+  const int d = d0 + lane;
+  const int dl = ch.valid ? d : a.dim - 1;
+  float h[NT];
+  if (a.K == 1) {
+    load_h0<NT, EXACT>(VL ? nullptr : a.h0, b, a.dim, dl, N, h);
+  } else {
+    // the groups before this one, composed: wave w folds a contiguous range
+    // of their aggregates, the ranges meet in LDS and every wave folds those
+    float xs = 0.0f, xh[NT];
+    int xf = 0;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) xh[n] = 0.0f;
+    if (j > 0) {
+      const int Kg = (a.K + G - 1) / G;
+      const int per = (j + G - 1) / G;
+      const int lo = w * per, hi = lo + per < j ? lo + per : j;
+      for (int i = lo; i < hi; ++i) {
+        const size_t slot = static_cast<size_t>(b) * Kg + i;
+        const WsSlot ws(a.ws_AS, a.ws_AH, slot, N, a.dim, d0);
+        const uint32_t vo = static_cast<uint32_t>(dl - d0) * 4;
+        append<NT, ACC>(ch, xs, xh, xf, ws.ld_s(vo),
+                        [&](int n) { return (EXACT || n < N) ? ws.ld_h(n, vo) : 0.0f; },
+                        __builtin_amdgcn_readfirstlane(a.ws_AF[slot]));
+      }
+      const GroupSlots<NT> slots(G);
+      slots.put(w, xs, xh, xf);
+      __syncthreads();
+      const int nw = (j + per - 1) / per;
+      xs = slots.s(0);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) xh[n] = slots.h(0, n);
+      xf = slots.f(0);
+      for (int i = 1; i < nw; ++i)
+        append<NT, ACC>(ch, xs, xh, xf, slots.s(i), [&](int n) { return slots.h(i, n); },
+                        slots.f(i));
+    }
+    // this chunk's prefix within the group (the identity at a group's first
+    // chunk); the first group's prefixes forget what came before them, so
+    // every composite above starts with a forgetting map and its H is the
+    // state entering the group
+#pragma unroll
+    for (int n = 0; n < NT; ++n) h[n] = xh[n];
+    if (c < a.K && (w > 0 || j == 0)) {
+      const size_t slot = static_cast<size_t>(b) * a.K + c;
+      const WsSlot ws(a.ws_S, a.ws_H, slot, N, a.dim, d0);
+      const uint32_t vo = static_cast<uint32_t>(dl - d0) * 4;
+      append<NT, ACC>(ch, xs, h, xf, ws.ld_s(vo),
+                      [&](int n) { return (EXACT || n < N) ? ws.ld_h(n, vo) : 0.0f; },
+                      __builtin_amdgcn_readfirstlane(a.ws_F[slot]));
+    }
+  }
+  if (c >= a.K) return;  // (after every barrier of the block)
   const int t_begin = c * a.Lc;
   const int len = (a.L - t_begin < a.Lc) ? a.L - t_begin : a.Lc;
   float S = 0.0f;
@@ -752,26 +1075,34 @@ void launch_carry(const float* A, const float* h0, const float* ws_S, float* ws_
                   const int* ws_F, int64_t batch, int dim, int N, int K, hipStream_t s);
 void launch_varlen_empty(const int* cu, int nseq, const float* h0, float* last_state, int dim,
                          int N, hipStream_t s);
+// Lets a kernel take `bytes` of dynamic LDS (once per kernel); 0 or an error.
+int allow_dynamic_lds(const void* kernel, size_t bytes);
 
 template <typename TA, int NT, bool EXACT, bool SP, bool GATE, bool VL>
 int launch_fwd(const FwdArgs<TA>& a, int64_t batch, hipStream_t s) {
   const unsigned tiles = static_cast<unsigned>((a.dim + 63) / 64);
+  const char* fn = VL ? "ssm_scan_fwd_varlen" : "ssm_scan_fwd";
+  const int G = a.K > 1 ? a.G : 1;
+  const size_t lds = a.K > 1 ? group_lds_bytes<NT>(G) : 0;
   if (a.K > 1) {
-    hipLaunchKernelGGL((fwd_agg_kernel<TA, NT, EXACT, SP, VL>),
-                       dim3(tiles, static_cast<unsigned>(a.K - 1), static_cast<unsigned>(batch)),
-                       dim3(64), 0, s, a);
-    launch_carry(a.A, VL ? nullptr : a.h0, a.ws_S, a.ws_H, VL ? a.ws_F : nullptr, batch, a.dim,
-                 a.N, a.K, s);
+    const void* ks = reinterpret_cast<const void*>(&fwd_sum_kernel<TA, NT, EXACT, SP, VL>);
+    const void* ko = reinterpret_cast<const void*>(&fwd_out_kernel<TA, NT, EXACT, SP, GATE, VL>);
+    if (allow_dynamic_lds(ks, lds) != 0 || allow_dynamic_lds(ko, lds) != 0)
+      return launch_status(fn);
+    const unsigned kga = static_cast<unsigned>((a.K - 1 + G - 1) / G);
+    hipLaunchKernelGGL((fwd_sum_kernel<TA, NT, EXACT, SP, VL>),
+                       dim3(tiles, kga, static_cast<unsigned>(batch)), dim3(64 * G), lds, s, a);
   }
-  if (!VL || a.L > 0)
-    hipLaunchKernelGGL((fwd_scan_kernel<TA, NT, EXACT, SP, GATE, VL>),
-                       dim3(tiles, static_cast<unsigned>(a.K), static_cast<unsigned>(batch)),
-                       dim3(64), 0, s, a);
+  if (!VL || a.L > 0) {
+    const unsigned kg = static_cast<unsigned>((a.K + G - 1) / G);
+    hipLaunchKernelGGL((fwd_out_kernel<TA, NT, EXACT, SP, GATE, VL>),
+                       dim3(tiles, kg, static_cast<unsigned>(batch)), dim3(64 * G), lds, s, a);
+  }
   // no tokens at all: every packed sequence's last_state is its initial state
   // (otherwise the output pass stores those of the empty ones)
   if (VL && a.L == 0 && a.last_state)
     launch_varlen_empty(a.cu, a.nseq, a.h0, a.last_state, a.dim, a.N, s);
-  return launch_status(VL ? "ssm_scan_fwd_varlen" : "ssm_scan_fwd");
+  return launch_status(fn);
 }
 
 // The state entering every chunk (summary and carry passes only; ws_H slot

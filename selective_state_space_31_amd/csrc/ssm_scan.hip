@@ -420,22 +420,26 @@ void launch_varlen_empty(const int* cu, int nseq, const float* h0, float* last_s
                      dim3(256), 0, s, cu, h0, last_state, dim, N);
 }
 
-// Chunking plan: enough (channel tile x chunk) waves for about kWavesPerSimd
-// resident waves on every SIMD, chunks of a multiple of 2*kGroup tokens and
-// at least kMinChunk long.
-#ifndef SSM_WAVES_PER_SIMD
-#define SSM_WAVES_PER_SIMD 8
-#endif
-#ifndef SSM_MIN_CHUNK
-#define SSM_MIN_CHUNK 32
-#endif
-constexpr int kWavesPerSimd = SSM_WAVES_PER_SIMD;
-constexpr int kMinChunk = SSM_MIN_CHUNK;
+// Chunking plan.  The sequence is cut into K chunks of Lc tokens (a multiple
+// of 2 kGroup), run as Kg = ceil(K / G) groups of G chunks, a workgroup of G
+// waves per (channel tile, group, sequence).  Every wave of a launch runs the
+// same number of tokens and the kernels are bound by their vector-ALU issue,
+// so a launch takes about as long as its busiest compute unit needs for its
+// share: ceil(workgroups / CUs) x G waves x (Lc + overhead) token-steps.  The
+// overhead counts the group compositions (a scan round or a prologue fold
+// each, ~0.3 token-steps) and the aggregate loads a prologue wave waits for
+// one after another (~0.3 token-steps each: other groups run meanwhile).
+// Splits that leave wave slots empty are charged for the idle share.  Measured on the 130M-, 2.8B-shaped
+// and long-context layers (chunk lengths 24-768, groups of 1-8), this picks
+// splits within ~1% of the fastest: 32-token chunks for the first,
+// 256-token chunks for the others.
+constexpr int kMinChunk = 32;
 static_assert(kMinChunk % (2 * kGroup) == 0, "chunks are whole pairs of token groups");
 
 struct Plan {
   int K;
   int Lc;
+  int G;
 };
 
 int device_cus() {
@@ -449,20 +453,96 @@ int device_cus() {
   return cus;
 }
 
-Plan plan_fwd(int64_t batch, int64_t L, int64_t dim) {
-  Plan p{1, static_cast<int>(L > 0 ? L : 1)};
-  const int64_t tiles = batch * ((dim + 63) / 64);
-  const int64_t target = static_cast<int64_t>(kWavesPerSimd) * 4 * device_cus();
-  if (L <= 0 || tiles >= target) return p;
-  int64_t K = (target + tiles - 1) / tiles;
+// Register width of the state the forward kernels run for dstate N.
+int fwd_width(int64_t N) {
+  if (N == 4 || N == 8 || N == 16 || N == 32) return static_cast<int>(N);
+  return N < 4 ? 4 : (N < 16 ? 16 : 64);
+}
+
+// Waves per SIMD the forward kernels of this width hold (as group_min_waves;
+// the wide states from their VGPRs).
+int fwd_waves_per_simd(int64_t N) {
+  const int nt = fwd_width(N);
+  if (nt <= 16) return nt == N ? 6 : 2;
+  return nt == 32 ? 4 : 1;
+}
+
+// Largest group for this width (as group_max).
+int fwd_group_max(int64_t N) {
+  const int nt = fwd_width(N);
+  return (nt == N && nt <= 32) ? 8 : 4;
+}
+
+// Estimated time (token-steps of the busiest compute unit) of a plan.
+double plan_cost(int64_t rows, int64_t K, int64_t Lc, int G, int cus, int64_t slots) {
+  const int64_t Kg = (K + G - 1) / G;
+  const int64_t wgs = rows * Kg;
+  int lg = 0;
+  while ((1 << lg) < G) ++lg;
+  const int64_t folds = Kg - 1 < G ? Kg - 1 : G;
+  const double over = K > 1 ? 0.3 * static_cast<double>(folds + lg + 1) +
+                                  0.3 * static_cast<double>((Kg - 1 + G - 1) / G)
+                            : 0.0;
+  const int64_t waves = rows * K;
+  const double idle = waves >= slots ? 1.0 : 1.0 + static_cast<double>(slots - waves) / slots;
+  return static_cast<double>((wgs + cus - 1) / cus) * G * (static_cast<double>(Lc) + over) * idle;
+}
+
+int64_t round_chunk(int64_t Lc) { return (Lc + 2 * kGroup - 1) / (2 * kGroup) * (2 * kGroup); }
+
+// The group size for a given split: 4 or 8 waves once there are 4 chunks
+// (smaller groups measured 6-80% slower: their prologues fold many group
+// aggregates one after another), the cheaper of the two with ties within 1%
+// going to 4; fewer chunks take one group of them all.
+Plan plan_groups(int64_t rows, int64_t K, int64_t Lc, int cus, int64_t slots, int gmax,
+                 double* cost_out) {
+  Plan best{static_cast<int>(K), static_cast<int>(Lc), 1};
+  if (K < 4 || gmax < 4) {
+    int G = 1;
+    while (G * 2 <= K && G * 2 <= gmax) G *= 2;
+    best.G = G;
+    if (cost_out) *cost_out = plan_cost(rows, K, Lc, G, cus, slots);
+    return best;
+  }
+  best.G = 4;
+  double bc = plan_cost(rows, K, Lc, 4, cus, slots);
+  if (gmax >= 8 && K >= 8) {
+    const double c = plan_cost(rows, K, Lc, 8, cus, slots);
+    if (c < bc * 0.99) {
+      bc = c;
+      best.G = 8;
+    }
+  }
+  if (cost_out) *cost_out = bc;
+  return best;
+}
+
+Plan plan_fwd(int64_t batch, int64_t L, int64_t dim, int64_t N, bool varlen) {
+  (void)varlen;
+  Plan p{1, static_cast<int>(L > 0 ? L : 1), 1};
+  const int64_t rows = batch * ((dim + 63) / 64);
+  const int cus = device_cus();
+  const int64_t slots = static_cast<int64_t>(4 * fwd_waves_per_simd(N)) * cus;
+  if (L <= 0 || rows >= slots || L < 2 * kMinChunk) return p;
+  const int gmax = fwd_group_max(N);
+  double bc = plan_cost(rows, 1, L, 1, cus, slots);
+  // splits from the one that just fills every wave slot up to four times it
   const int64_t kmax = L / kMinChunk;
-  if (K > kmax) K = kmax;
-  if (K <= 1) return p;
-  int64_t Lc = (L + K - 1) / K;
-  Lc = (Lc + 2 * kGroup - 1) / (2 * kGroup) * (2 * kGroup);
-  K = (L + Lc - 1) / Lc;
-  p.K = static_cast<int>(K);
-  p.Lc = static_cast<int>(Lc);
+  int64_t k0 = (slots + rows - 1) / rows;
+  k0 = k0 < kmax ? k0 : kmax;
+  int64_t last_lc = -1;
+  for (int64_t K = k0 < 2 ? 2 : k0; K <= 4 * k0 && K <= kmax; ++K) {
+    const int64_t Lc = round_chunk((L + K - 1) / K);
+    if (Lc == last_lc) continue;
+    last_lc = Lc;
+    const int64_t Kc = (L + Lc - 1) / Lc;
+    double c;
+    const Plan q = plan_groups(rows, Kc, Lc, cus, slots, gmax, &c);
+    if (c < bc * 0.999) {
+      bc = c;
+      p = q;
+    }
+  }
   return p;
 }
 
@@ -470,30 +550,54 @@ Plan plan_fwd(int64_t batch, int64_t L, int64_t dim) {
 // whole pairs of token groups; one chunk (no workspace) when it covers the
 // sequence.  K above kMaxChunks is refused by the caller.
 constexpr int64_t kMaxChunks = 65535;  // chunks per sequence: one grid dimension
-Plan plan_fwd_chunked(int64_t L, int64_t chunk_len) {
-  Plan p{1, static_cast<int>(L > 0 ? L : 1)};
-  const int64_t Lc = (chunk_len + 2 * kGroup - 1) / (2 * kGroup) * (2 * kGroup);
+Plan plan_fwd_chunked(int64_t batch, int64_t L, int64_t dim, int64_t N, bool varlen,
+                      int64_t chunk_len) {
+  (void)varlen;
+  Plan p{1, static_cast<int>(L > 0 ? L : 1), 1};
+  const int64_t Lc = round_chunk(chunk_len);
   if (L <= 0 || Lc >= L) return p;
   const int64_t K = (L + Lc - 1) / Lc;
-  p.K = static_cast<int>(K < kMaxChunks + 1 ? K : kMaxChunks + 1);
-  p.Lc = static_cast<int>(Lc);
-  return p;
+  if (K > kMaxChunks) {
+    p.K = static_cast<int>(kMaxChunks + 1);
+    return p;
+  }
+  const int cus = device_cus();
+  return plan_groups(batch * ((dim + 63) / 64), K, Lc, cus,
+                     static_cast<int64_t>(4 * fwd_waves_per_simd(N)) * cus, fwd_group_max(N),
+                     nullptr);
 }
 
-// Workspace: ws_S (batch, K-1, dim), then ws_H (batch, K, N, dim), then ws_F
-// (K-1 ints, packed sequences only), each part 256-byte aligned.
+// Workspace of the grouped forward, each part 256-byte aligned:
+//   E: every chunk's exclusive prefix within its group, S (batch, K, dim),
+//      H (batch, K, N, dim), F (batch, K) int;
+//   A: every group's aggregate, S (batch, Kg, dim), H (batch, Kg, N, dim),
+//      F (batch, Kg) int.
 struct WsLayout {
-  size_t s_off, h_off, f_off, total;
+  size_t es, eh, ef, as, ah, af, total;
 };
 
-WsLayout workspace_layout(int64_t batch, int64_t dim, int64_t N, const Plan& p, bool varlen) {
-  WsLayout w{0, 0, 0, 0};
+WsLayout workspace_layout(int64_t batch, int64_t dim, int64_t N, const Plan& p) {
+  WsLayout w{0, 0, 0, 0, 0, 0, 0};
   if (p.K <= 1) return w;
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-  w.h_off = up(static_cast<size_t>(batch) * (p.K - 1) * dim * 4);
-  w.f_off = up(w.h_off + static_cast<size_t>(batch) * p.K * N * dim * 4);
-  w.total = varlen ? w.f_off + static_cast<size_t>(p.K - 1) * 4 : w.f_off;
+  const size_t K = static_cast<size_t>(p.K), Kg = static_cast<size_t>((p.K + p.G - 1) / p.G);
+  const size_t B = static_cast<size_t>(batch), D = static_cast<size_t>(dim), n = static_cast<size_t>(N);
+  w.eh = up(B * K * D * 4);
+  w.ef = up(w.eh + B * K * n * D * 4);
+  w.as = up(w.ef + B * K * 4);
+  w.ah = up(w.as + B * Kg * D * 4);
+  w.af = up(w.ah + B * Kg * n * D * 4);
+  w.total = up(w.af + B * Kg * 4);
   return w;
+}
+
+// Dynamic LDS above the default per-launch allowance needs the kernel's
+// attribute raised once.
+int allow_dynamic_lds(const void* kernel, size_t bytes) {
+  if (bytes <= 64 * 1024) return 0;
+  const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(bytes));
+  return e == hipSuccess ? 0 : -1;
 }
 
 template <typename TA, bool VL>
@@ -575,6 +679,10 @@ int fwd_impl(const char* fn, const void* x, const void* delta, const float* delt
   if (dim > kMaxDim || batch > 65535 || seqlen > kMaxLen)
     return fail(SSM_ERR_SHAPE, "%s: dim %lld, batch %lld or seqlen %lld too large", fn,
                 (long long)dim, (long long)batch, (long long)seqlen);
+  // a chunk summary's dim x dstate floats are addressed with 32-bit offsets
+  if (dim * dstate >= (int64_t{1} << 29))
+    return fail(SSM_ERR_SHAPE, "%s: dim x dstate = %lld is 2^29 or more", fn,
+                (long long)(dim * dstate));
   if (seqlen > 0 && (!x || !delta || !B || !C || !out))
     return fail(SSM_ERR_NULL, "%s: x, delta, B, C and out are required", fn);
   if (!A) return fail(SSM_ERR_NULL, "%s: A is required", fn);
@@ -607,11 +715,12 @@ int fwd_impl(const char* fn, const void* x, const void* delta, const float* delt
   if (overlap(outs[0], outs[1])) return fail(SSM_ERR_ALIAS, "%s: out overlaps last_state", fn);
   if (chunk_len < 0)
     return fail(SSM_ERR_SHAPE, "%s: chunk_len must be >= 0, got %lld", fn, (long long)chunk_len);
-  const Plan plan = chunk_len > 0 ? plan_fwd_chunked(seqlen, chunk_len) : plan_fwd(batch, seqlen, dim);
+  const Plan plan = chunk_len > 0 ? plan_fwd_chunked(batch, seqlen, dim, dstate, varlen, chunk_len)
+                                  : plan_fwd(batch, seqlen, dim, dstate, varlen);
   if (plan.K > kMaxChunks)
     return fail(SSM_ERR_SHAPE, "%s: chunk_len %lld cuts seqlen %lld into more than %lld chunks", fn,
                 (long long)chunk_len, (long long)seqlen, (long long)kMaxChunks);
-  const WsLayout wl = workspace_layout(batch, dim, dstate, plan, varlen);
+  const WsLayout wl = workspace_layout(batch, dim, dstate, plan);
   if (workspace_bytes < wl.total || (wl.total > 0 && !workspace))
     return fail(SSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, wl.total,
                 workspace_bytes);
@@ -625,24 +734,25 @@ int fwd_impl(const char* fn, const void* x, const void* delta, const float* delt
       return fail(SSM_ERR_ALIAS, "%s: workspace overlaps input %s", fn, i.name);
   if (seqlen == 0 && !last_state) return SSM_OK;
   char* wsb = static_cast<char*>(workspace);
-  float* ws_S = wl.total ? reinterpret_cast<float*>(wsb + wl.s_off) : nullptr;
-  float* ws_H = wl.total ? reinterpret_cast<float*>(wsb + wl.h_off) : nullptr;
-  int* ws_F = (wl.total && varlen) ? reinterpret_cast<int*>(wsb + wl.f_off) : nullptr;
+  auto wf = [&](size_t off) { return wl.total ? reinterpret_cast<float*>(wsb + off) : nullptr; };
+  auto wi = [&](size_t off) { return wl.total ? reinterpret_cast<int*>(wsb + off) : nullptr; };
   const int nq = static_cast<int>(varlen ? nseq : 0);
 
   if (dtype == SSM_DTYPE_F32) {
     FwdArgs<float> a{static_cast<const float*>(x), static_cast<const float*>(delta), delta_bias, A,
                      static_cast<const float*>(B), static_cast<const float*>(C), D_skip,
                      static_cast<const float*>(z), static_cast<float*>(out), last_state,
-                     initial_state, ws_S, ws_H, ws_F, cu, nq, static_cast<int>(seqlen), plan.Lc,
-                     plan.K, static_cast<int>(dim), static_cast<int>(dstate)};
+                     initial_state, wf(wl.es), wf(wl.eh), wi(wl.ef), cu, nq,
+                     static_cast<int>(seqlen), plan.Lc, plan.K, static_cast<int>(dim),
+                     static_cast<int>(dstate), plan.G, wf(wl.as), wf(wl.ah), wi(wl.af)};
     return dispatch_fwd(a, batch, delta_softplus != 0, stream);
   }
   FwdArgs<bf16_t> a{static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(delta), delta_bias, A,
                     static_cast<const bf16_t*>(B), static_cast<const bf16_t*>(C), D_skip,
                     static_cast<const bf16_t*>(z), static_cast<bf16_t*>(out), last_state,
-                    initial_state, ws_S, ws_H, ws_F, cu, nq, static_cast<int>(seqlen), plan.Lc,
-                    plan.K, static_cast<int>(dim), static_cast<int>(dstate)};
+                    initial_state, wf(wl.es), wf(wl.eh), wi(wl.ef), cu, nq,
+                    static_cast<int>(seqlen), plan.Lc, plan.K, static_cast<int>(dim),
+                    static_cast<int>(dstate), plan.G, wf(wl.as), wf(wl.ah), wi(wl.af)};
   return dispatch_fwd(a, batch, delta_softplus != 0, stream);
 }
 
@@ -705,7 +815,7 @@ size_t ssm_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
   if (batch < 1 || dim < 1 || seqlen < 0 || dstate < 1 || dstate > 64 || dim > kMaxDim ||
       batch > 65535 || seqlen > kMaxLen)
     return 0;
-  return workspace_layout(batch, dim, dstate, plan_fwd(batch, seqlen, dim), false).total;
+  return workspace_layout(batch, dim, dstate, plan_fwd(batch, seqlen, dim, dstate, false)).total;
 }
 
 size_t ssm_scan_fwd_varlen_workspace_bytes(int64_t nseq, int64_t total_len, int64_t dim,
@@ -714,7 +824,7 @@ size_t ssm_scan_fwd_varlen_workspace_bytes(int64_t nseq, int64_t total_len, int6
   if (nseq < 1 || nseq > kMaxSeqs || dim < 1 || total_len < 0 || dstate < 1 || dstate > 64 ||
       dim > kMaxDim || total_len > kMaxLen)
     return 0;
-  return workspace_layout(1, dim, dstate, plan_fwd(1, total_len, dim), true).total;
+  return workspace_layout(1, dim, dstate, plan_fwd(1, total_len, dim, dstate, true)).total;
 }
 
 int ssm_scan_fwd(const void* x, const void* delta, const float* delta_bias, int delta_softplus,
@@ -757,9 +867,9 @@ size_t ssm_scan_fwd_chunked_workspace_bytes(int64_t batch, int64_t seqlen, int64
   if (batch < 1 || dim < 1 || seqlen < 0 || dstate < 1 || dstate > 64 || dim > kMaxDim ||
       batch > 65535 || seqlen > kMaxLen)
     return 0;
-  const Plan p = plan_fwd_chunked(seqlen, chunk_len);
+  const Plan p = plan_fwd_chunked(batch, seqlen, dim, dstate, false, chunk_len);
   if (p.K > kMaxChunks) return 0;
-  return workspace_layout(batch, dim, dstate, p, false).total;
+  return workspace_layout(batch, dim, dstate, p).total;
 }
 
 int ssm_scan_fwd_chunked(const void* x, const void* delta, const float* delta_bias,

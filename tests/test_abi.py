@@ -57,9 +57,9 @@ def test_workspace_query_is_host_only(lib):
     assert lib.ssm_scan_fwd_varlen_workspace_bytes(6, 8192, 1536, 16, 1) > 0
     assert lib.ssm_scan_fwd_varlen_workspace_bytes(0, 8192, 1536, 16, 1) == 0
     assert lib.ssm_scan_fwd_varlen_workspace_bytes(6, -1, 1536, 16, 1) == 0
-    # packed sequences need the per-chunk flags on top of the dense layout
+    # packed sequences run as one row of the dense layout: the same summaries
     assert (lib.ssm_scan_fwd_varlen_workspace_bytes(3, 8192, 1536, 16, 1)
-            > lib.ssm_scan_fwd_workspace_bytes(1, 8192, 1536, 16, 1))
+            == lib.ssm_scan_fwd_workspace_bytes(1, 8192, 1536, 16, 1))
 
 
 def test_chunked_workspace_query(lib):
@@ -96,11 +96,14 @@ def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
     host, before the scratch is looked up or anything is enqueued."""
     P = ctypes.c_void_p
     f = lambda k: P(0x10000000000 * k)
-    # batch 1, 1024 channels, 2^20 tokens: chunk summaries of well over 64 MiB
-    need = lib.ssm_scan_fwd_workspace_bytes(1, 1 << 20, 1024, 64, 0)
-    assert need > 64 << 20
+    # a shape whose chunk summaries need more than 64 MiB under the library's plan
+    shapes = [(b, L, d, n) for n in (32, 16, 64) for d in (5120, 8192, 4096, 2048)
+              for L in (1 << 14, 1 << 21) for b in (3, 8, 2, 1)]
+    big = [s for s in shapes if lib.ssm_scan_fwd_workspace_bytes(*s, 0) > 64 << 20]
+    assert big, "no candidate shape exceeds the scratch"
+    b, L, d, n = big[0]
     rc = lib.ssm_scan_fwd_noalloc(f(1), f(2), None, 1, f(3), f(4), f(5), None, None, f(6), None,
-                                  None, 1, 1 << 20, 1024, 64, 0, None)
+                                  None, b, L, d, n, 0, None)
     assert rc == -6
     assert b"scratch" in lib.ssm_last_error()
 
