@@ -23,7 +23,6 @@ matrix cores), each with its own roofline.
                   [--no-secondary] [--only WORKLOAD]
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -42,18 +41,6 @@ MALL_BYTES = 256 << 20      # Infinity Cache (last-level) capacity
 WORKLOAD = "longctx_bf16"
 METRIC = "selective-scan fwd tokens·channels/s + achieved HBM GB/s (% of peak), 1 GPU"
 COUNTERS_DIR = os.path.join(ROOT, "profiles")
-CSRC = os.path.join(ROOT, "selective_state_space_31_amd", "csrc")
-
-
-def kernel_source_hash():
-    """Hash of the library's kernel sources, recorded with the rocprofv3
-    counters so that counters taken on other code are never reported."""
-    h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def counters_entry(workload):
@@ -66,7 +53,8 @@ def counters_entry(workload):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    from selective_state_space_31_amd.counters import source_hash
+    if t.get("kernel_source_sha256_16") != source_hash(workload):
         return None
     return t
 

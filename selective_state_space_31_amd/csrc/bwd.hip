@@ -6,16 +6,17 @@
 // them, stripe by stripe (recomputation in the backward pass, as the page
 // cited in the header describes for the original kernel).  Plan, for
 // stripes of Ls <= 32 tokens:
-//   1. forward summary + carry passes (the forward's own kernels) give the
-//      state entering every stripe;
-//   2. adjoint summaries: per stripe, walked from its last token to its
-//      first from a zero adjoint, a <- (a + C_t dy_t) * e^(dt_t A), with the
-//      stripe's sum of Delta; the adjoint recurrence is linear with the same
-//      decays as the state, so
-//   3. the forward's carry kernel, fed the stripes in reverse order and
-//      started from dlast_state, gives the adjoint flowing into every
-//      stripe's last token from the tokens after it;
-//   4. main pass: per stripe, SPL = min(N, 8) states per lane (N/SPL lanes
+//   1. summaries, one launch for both: per stripe, the state it reaches
+//      from zero with its sum of Delta (the forward's chunk summary), and the
+//      adjoint walked from its last token to its first from a zero adjoint,
+//      a <- (a + C_t dy_t) * e^(dt_t A); the adjoint recurrence is linear
+//      with the same decays as the state, so
+//   2. one carry launch folds both chains: the states from the initial
+//      state in stripe order, the adjoints from dlast_state in reverse
+//      stripe order, giving the state entering every stripe and the
+//      adjoint flowing into every stripe's last token from the tokens after
+//      it;
+//   3. main pass: per stripe, SPL = min(N, 8) states per lane (N/SPL lanes
 //      per channel).  The lane runs its stripe forward from the entering
 //      state, keeping a checkpoint of its states every SUB = 64/SPL tokens,
 //      then takes the sub-chunks from last to first: recompute the
@@ -25,7 +26,7 @@
 //      are reduced across the wave's channels by lane shuffles and across
 //      the workgroup's 4 waves in LDS into one partial per workgroup;
 //      dA, dD, dbias are accumulated per stripe;
-//   5. a reduction pass adds the partials in a fixed order (no atomics: the
+//   4. a reduction pass adds the partials in a fixed order (no atomics: the
 //      result is bitwise reproducible run to run).
 #include <hip/hip_runtime.h>
 
@@ -37,13 +38,6 @@
 #include "kernels.hpp"
 
 namespace ssm {
-
-#define SSM_BWD_STATE_INSTANCES(X) \
-  X(float, 4) X(float, 8) X(float, 16) X(bf16_t, 4) X(bf16_t, 8) X(bf16_t, 16)
-#define SSM_EXTERN_STATES(TA, NT)                                                           \
-  extern template int launch_fwd_states<TA, NT, true>(const FwdArgs<TA>&, int64_t, bool, \
-                                                      hipStream_t);
-SSM_BWD_STATE_INSTANCES(SSM_EXTERN_STATES)
 
 constexpr int kBwdStripe = 32;     // tokens per stripe at most (a multiple of 16)
 constexpr int kBwdThreads = 256;   // main pass workgroup: 4 waves of the same stripe
@@ -99,14 +93,12 @@ __device__ __forceinline__ float sigmoid_f32(float u) {
 }
 
 // ----------------------------------------------------------------------------
-// 2. adjoint summaries: block (64 channels, stripe c = 1..K-1, sequence)
+// 1. adjoint summary of stripe c = 1..K-1 of sequence b (one wave, 64 channels)
 // ----------------------------------------------------------------------------
 template <typename TA, int NT, bool SP, bool GATE>
-__global__ void __launch_bounds__(64) bwd_agg_kernel(BwdArgs<TA> a) {
+__device__ __forceinline__ void bwd_agg_block(const BwdArgs<TA>& a, int tile, int c, int64_t b) {
   const int lane = threadIdx.x;
-  const int d = blockIdx.x * 64 + lane;
-  const int c = blockIdx.y + 1;
-  const int64_t b = blockIdx.z;
+  const int d = tile * 64 + lane;
   const bool valid = d < a.dim;
   const int dl = valid ? d : a.dim - 1;
   float a2[NT], adj[NT];
@@ -170,8 +162,21 @@ __global__ void __launch_bounds__(64) bwd_agg_kernel(BwdArgs<TA> a) {
   }
 }
 
+// Step 1 in one launch: block (x, stripe, sequence) of one wave; the
+// first `tiles` x-blocks summarise the states of stripe y (the forward's
+// chunk summary), the others the adjoints of stripe y+1.
+template <typename TA, int NT, bool SP, bool GATE>
+__global__ void __launch_bounds__(64) bwd_sums_kernel(BwdArgs<TA> a, FwdArgs<TA> f) {
+  const int tiles = (a.dim + 63) / 64;
+  const int x = static_cast<int>(blockIdx.x);
+  if (x < tiles)
+    fwd_agg_block<TA, NT, SP>(f, x, static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.z));
+  else
+    bwd_agg_block<TA, NT, SP, GATE>(a, x - tiles, static_cast<int>(blockIdx.y) + 1, blockIdx.z);
+}
+
 // ----------------------------------------------------------------------------
-// 4. main pass
+// 3. main pass
 // ----------------------------------------------------------------------------
 // Sum over the G lanes of one channel (adjacent lanes of a quad): DPP quad
 // permutations, no LDS traffic.
@@ -385,7 +390,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
     for (int j = 0; j < SPL; ++j) hout[j] = __builtin_fmaf(dA[j], hin[j], dx * Bv[j]);
   };
 
-  // 4a. forward over the stripe with a checkpoint every SUB tokens (in LDS:
+  // 3a. forward over the stripe with a checkpoint every SUB tokens (in LDS:
   // each lane reads back only its own); the state after the last sub-chunk
   // is not needed.  With several lanes per channel, every token's dt is also
   // kept in LDS (both lanes write the same value; each reads it back), so
@@ -413,7 +418,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
     }
   }
 
-  // 4b. adjoint flowing into the stripe's last token from later tokens
+  // 3b. adjoint flowing into the stripe's last token from later tokens
   float adj[SPL];
 #pragma unroll
   for (int j = 0; j < SPL; ++j) {
@@ -429,7 +434,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
   for (int j = 0; j < SPL; ++j) dAacc[j] = 0.0f;
   float dDacc = 0.0f, dbacc = 0.0f;
 
-  // 4c. sub-chunks from last to first (nsub is uniform over the workgroup)
+  // 3c. sub-chunks from last to first (nsub is uniform over the workgroup)
   for (int k = nsub - 1; k >= 0; --k) {
     const int t0 = s + k * SUB;
     const int t1 = (t0 + SUB < e) ? t0 + SUB : e;
@@ -559,7 +564,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_main_kernel(BwdArgs<TA> a) {
 }
 
 // ----------------------------------------------------------------------------
-// 5. reductions of the partials, in a fixed order
+// 4. reductions of the partials, in a fixed order
 // ----------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(const float* __restrict__ pB,
                                                            const float* __restrict__ pC,
@@ -725,31 +730,29 @@ BwdWs bwd_layout(int64_t batch, int64_t L, int64_t dim, int64_t N, const BwdPlan
 template <typename TA, int NT>
 int launch_bwd(const BwdArgs<TA>& a, const FwdArgs<TA>& f, bool sp, bool gate, float* dA,
                float* dB, float* dC, float* dD, float* dbias, hipStream_t s) {
-  // 1. entering states
-  int rc = launch_fwd_states<TA, NT, true>(f, a.batch, sp, s);
-  if (rc != SSM_OK) return rc;
-  // 2-3. adjoint summaries and their carry
-#define SSM_BWD_LAUNCH(KERN, GRID, BLOCK)                                                       \
+#define SSM_BWD_LAUNCH(KERN, GRID, BLOCK, ...)                                                 \
   do {                                                                                          \
-    if (sp && gate) hipLaunchKernelGGL((KERN<TA, NT, true, true>), GRID, BLOCK, 0, s, a);       \
-    else if (sp) hipLaunchKernelGGL((KERN<TA, NT, true, false>), GRID, BLOCK, 0, s, a);         \
-    else if (gate) hipLaunchKernelGGL((KERN<TA, NT, false, true>), GRID, BLOCK, 0, s, a);       \
-    else hipLaunchKernelGGL((KERN<TA, NT, false, false>), GRID, BLOCK, 0, s, a);                \
+    if (sp && gate) hipLaunchKernelGGL((KERN<TA, NT, true, true>), GRID, BLOCK, 0, s, __VA_ARGS__); \
+    else if (sp) hipLaunchKernelGGL((KERN<TA, NT, true, false>), GRID, BLOCK, 0, s, __VA_ARGS__);   \
+    else if (gate) hipLaunchKernelGGL((KERN<TA, NT, false, true>), GRID, BLOCK, 0, s, __VA_ARGS__); \
+    else hipLaunchKernelGGL((KERN<TA, NT, false, false>), GRID, BLOCK, 0, s, __VA_ARGS__);          \
   } while (0)
   if (a.K > 1) {
-    const dim3 grid(static_cast<unsigned>((a.dim + 63) / 64), static_cast<unsigned>(a.K - 1),
-                    static_cast<unsigned>(a.batch));
-    SSM_BWD_LAUNCH(bwd_agg_kernel, grid, dim3(64));
-    launch_carry(f.A, a.dlast, a.rS, a.rH, nullptr, a.batch, a.dim, NT, a.K, s);
+    // 1-2. summaries of states and adjoints, then both carries in one launch
+    const unsigned tiles = static_cast<unsigned>((a.dim + 63) / 64);
+    const dim3 grid(2 * tiles, static_cast<unsigned>(a.K - 1), static_cast<unsigned>(a.batch));
+    SSM_BWD_LAUNCH(bwd_sums_kernel, grid, dim3(64), a, f);
+    launch_carry(f.A, CarryChain{f.h0, f.ws_S, f.ws_H}, CarryChain{a.dlast, a.rS, a.rH}, a.batch,
+                 a.dim, NT, a.K, s);
   }
-  // 4. main pass
+  // 3. main pass
   {
     const dim3 grid(static_cast<unsigned>(a.tiles), static_cast<unsigned>(a.K),
                     static_cast<unsigned>(a.batch));
-    SSM_BWD_LAUNCH(bwd_main_kernel, grid, dim3(kBwdThreads));
+    SSM_BWD_LAUNCH(bwd_main_kernel, grid, dim3(kBwdThreads), a);
   }
 #undef SSM_BWD_LAUNCH
-  // 5. reductions
+  // 4. reductions
   const int64_t per = a.batch * a.L * NT;
   hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(static_cast<unsigned>((per + 255) / 256)), dim3(256),
                      0, s, a.pB, a.pC, dB, dC, per, a.tiles);

@@ -617,55 +617,35 @@ __device__ __forceinline__ void load_h0(const float* h0, int s, int dim, int dl,
   for (int n = 0; n < NT; ++n) h[n] = (hp && (EXACT || n < N)) ? hp[n] : 0.0f;
 }
 
-// Summary pass: block (channel tile, chunk c < K-1, sequence b).  With
-// packed sequences, a chunk in which a sequence starts is summarised from
-// its last start: the state there is that sequence's initial state, and
-// the chunk's end state no longer depends on the state entering it.
-template <typename TA, int NT, bool EXACT, bool SP, bool VL>
-__global__ void __launch_bounds__(64) fwd_agg_kernel(FwdArgs<TA> a) {
-  const int d0 = blockIdx.x * 64;
-  const int c = blockIdx.y;
-  const int b = blockIdx.z;
-  const Chan<NT> ch = load_chan<TA, NT, EXACT>(a, d0);
-  const int dl = ch.valid ? d0 + static_cast<int>(threadIdx.x) : a.dim - 1;
+// Summary of chunk c < K-1 of sequence b for the wave's 64 channels (one
+// wave per block), stored for the carry: the sum of Delta over the chunk in
+// ws_S slot c and the state the chunk reaches from zero in ws_H slot c+1.
+// The backward recomputes the states entering its stripes from these.
+template <typename TA, int NT, bool SP>
+__device__ __forceinline__ void fwd_agg_block(const FwdArgs<TA>& a, int tile, int c, int b) {
+  const int d0 = tile * 64;
+  const Chan<NT> ch = load_chan<TA, NT, true>(a, d0);
   float h[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) h[n] = 0.0f;
   float S = 0.0f;
   const int t_begin = c * a.Lc;  // chunks before the last are full (Lc is a multiple of 2*kGroup)
-  bool reset = false;
-  if constexpr (VL) {
-    const int t_end = t_begin + a.Lc;
-    const int s = seq_owner(a.cu, a.nseq, t_end - 1);
-    const int st = a.cu[s];
-    if (st >= t_begin && st < t_end) {
-      reset = true;
-      load_h0<NT, EXACT>(a.h0, s, a.dim, dl, a.N, h);
-      if (ch.pow)
-        run_tokens<TA, NT, EXACT, SP, false, true, true>(a, ch, b, st, t_end - st, h, S);
-      else
-        run_tokens<TA, NT, EXACT, SP, false, false, true>(a, ch, b, st, t_end - st, h, S);
-    }
-  }
-  if (!reset) {
-    constexpr bool REV = EXACT && NT <= 16 && sizeof(TA) == 2 && (sizeof(TA) * NT) % 4 == 0;
-    if (ch.pow) {
-      if constexpr (REV)
-        agg_reverse<TA, NT, SP>(a, ch, b, t_begin, a.Lc, h, S);
-      else
-        run_tokens<TA, NT, EXACT, SP, false, true, true>(a, ch, b, t_begin, a.Lc, h, S);
-    } else
-      run_tokens<TA, NT, EXACT, SP, false, false, true>(a, ch, b, t_begin, a.Lc, h, S);
+  constexpr bool REV = NT <= 16 && sizeof(TA) == 2 && (sizeof(TA) * NT) % 4 == 0;
+  if (ch.pow) {
+    if constexpr (REV)
+      agg_reverse<TA, NT, SP>(a, ch, b, t_begin, a.Lc, h, S);
+    else
+      run_tokens<TA, NT, true, SP, false, true, true>(a, ch, b, t_begin, a.Lc, h, S);
+  } else {
+    run_tokens<TA, NT, true, SP, false, false, true>(a, ch, b, t_begin, a.Lc, h, S);
   }
   if (ch.valid) {
     const int d = d0 + threadIdx.x;
     a.ws_S[(static_cast<size_t>(b) * (a.K - 1) + c) * a.dim + d] = S;
     const size_t slot = static_cast<size_t>(b) * a.K + c + 1;
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      if (EXACT || n < a.N) a.ws_H[(slot * a.N + n) * a.dim + d] = h[n];
+    for (int n = 0; n < NT; ++n) a.ws_H[(slot * a.N + n) * a.dim + d] = h[n];
   }
-  if (VL && blockIdx.x == 0 && threadIdx.x == 0) a.ws_F[c] = reset ? 1 : 0;
 }
 
 // ----------------------------------------------------------------------------
@@ -673,7 +653,7 @@ __global__ void __launch_bounds__(64) fwd_agg_kernel(FwdArgs<TA> a) {
 //
 // Chunks are taken in groups of G consecutive ones, a workgroup of G waves
 // per (channel tile, group, sequence), one wave per chunk.
-//   fwd_sum_kernel : each wave summarises its chunk (as fwd_agg_kernel), the
+//   fwd_sum_kernel : each wave summarises its chunk (as fwd_agg_block), the
 //                    group's waves scan their summaries in LDS (inclusive,
 //                    log2 G rounds of the composition), and leave each
 //                    chunk's exclusive prefix within the group and the
@@ -963,6 +943,27 @@ __global__ void __launch_bounds__(64 * group_max(NT, EXACT), group_min_waves(NT,
   if (a.K == 1) {
     load_h0<NT, EXACT>(VL ? nullptr : a.h0, b, a.dim, dl, N, h);
   } else {
+    // This chunk's prefix within the group (the identity at a group's first
+    // chunk).  With 16-bit activations it is loaded first, its loads in flight
+    // during the fold below (float32 activations leave no registers for it).
+    constexpr bool HOIST = sizeof(TA) == 2;
+    const bool own = c < a.K && (w > 0 || j == 0);
+    const uint32_t vo = static_cast<uint32_t>(dl - d0) * 4;
+    const size_t own_slot = static_cast<size_t>(b) * a.K + c;
+    float ps = 0.0f, ph[NT];
+    int pf = 0;
+    if constexpr (HOIST) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) ph[n] = 0.0f;
+      if (own) {
+        const WsSlot ws(a.ws_S, a.ws_H, own_slot, N, a.dim, d0);
+        ps = ws.ld_s(vo);
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          if (EXACT || n < N) ph[n] = ws.ld_h(n, vo);
+        pf = __builtin_amdgcn_readfirstlane(a.ws_F[own_slot]);
+      }
+    }
     // the groups before this one, composed: wave w folds a contiguous range
     // of their aggregates, the ranges meet in LDS and every wave folds those
     float xs = 0.0f, xh[NT];
@@ -976,7 +977,6 @@ __global__ void __launch_bounds__(64 * group_max(NT, EXACT), group_min_waves(NT,
       for (int i = lo; i < hi; ++i) {
         const size_t slot = static_cast<size_t>(b) * Kg + i;
         const WsSlot ws(a.ws_AS, a.ws_AH, slot, N, a.dim, d0);
-        const uint32_t vo = static_cast<uint32_t>(dl - d0) * 4;
         append<NT, ACC>(ch, xs, xh, xf, ws.ld_s(vo),
                         [&](int n) { return (EXACT || n < N) ? ws.ld_h(n, vo) : 0.0f; },
                         __builtin_amdgcn_readfirstlane(a.ws_AF[slot]));
@@ -993,19 +993,20 @@ __global__ void __launch_bounds__(64 * group_max(NT, EXACT), group_min_waves(NT,
         append<NT, ACC>(ch, xs, xh, xf, slots.s(i), [&](int n) { return slots.h(i, n); },
                         slots.f(i));
     }
-    // this chunk's prefix within the group (the identity at a group's first
-    // chunk); the first group's prefixes forget what came before them, so
-    // every composite above starts with a forgetting map and its H is the
-    // state entering the group
+    // the first group's prefixes forget what came before them, so every
+    // composite above starts with a forgetting map and its H is the state
+    // entering the group
 #pragma unroll
     for (int n = 0; n < NT; ++n) h[n] = xh[n];
-    if (c < a.K && (w > 0 || j == 0)) {
-      const size_t slot = static_cast<size_t>(b) * a.K + c;
-      const WsSlot ws(a.ws_S, a.ws_H, slot, N, a.dim, d0);
-      const uint32_t vo = static_cast<uint32_t>(dl - d0) * 4;
-      append<NT, ACC>(ch, xs, h, xf, ws.ld_s(vo),
-                      [&](int n) { return (EXACT || n < N) ? ws.ld_h(n, vo) : 0.0f; },
-                      __builtin_amdgcn_readfirstlane(a.ws_F[slot]));
+    if (own) {
+      if constexpr (HOIST) {
+        append<NT, ACC>(ch, xs, h, xf, ps, [&](int n) { return ph[n]; }, pf);
+      } else {
+        const WsSlot ws(a.ws_S, a.ws_H, own_slot, N, a.dim, d0);
+        append<NT, ACC>(ch, xs, h, xf, ws.ld_s(vo),
+                        [&](int n) { return (EXACT || n < N) ? ws.ld_h(n, vo) : 0.0f; },
+                        __builtin_amdgcn_readfirstlane(a.ws_F[own_slot]));
+      }
     }
   }
   if (c >= a.K) return;  // (after every barrier of the block)
@@ -1071,8 +1072,15 @@ __global__ void __launch_bounds__(64 * group_max(NT, EXACT), group_min_waves(NT,
 // launchers (host side of the templates above)
 // ----------------------------------------------------------------------------
 int launch_status(const char* what);
-void launch_carry(const float* A, const float* h0, const float* ws_S, float* ws_H,
-                  const int* ws_F, int64_t batch, int dim, int N, int K, hipStream_t s);
+// Chained carries over K-1 chunk summaries, one or two independent chains
+// (the second's pointers null for one); see fwd_carry_kernel.
+struct CarryChain {
+  const float* h0;    // (batch, dim, N) state entering chunk 0, or null (zeros)
+  const float* ws_S;  // (batch, K-1, dim) sums of Delta
+  float* ws_H;        // (batch, K, N, dim): slot c+1 summary of chunk c in, entering state out
+};
+void launch_carry(const float* A, const CarryChain& c0, const CarryChain& c1, int64_t batch,
+                  int dim, int N, int K, hipStream_t s);
 void launch_varlen_empty(const int* cu, int nseq, const float* h0, float* last_state, int dim,
                          int N, hipStream_t s);
 // Lets a kernel take `bytes` of dynamic LDS (once per kernel); 0 or an error.
@@ -1107,19 +1115,6 @@ int launch_fwd(const FwdArgs<TA>& a, int64_t batch, hipStream_t s) {
 
 // The state entering every chunk (summary and carry passes only; ws_H slot
 // c holds it for c >= 1 afterwards), for the backward's recomputation.
-template <typename TA, int NT, bool EXACT>
-int launch_fwd_states(const FwdArgs<TA>& a, int64_t batch, bool sp, hipStream_t s) {
-  if (a.K <= 1) return launch_status("ssm_scan_bwd");
-  const dim3 grid(static_cast<unsigned>((a.dim + 63) / 64), static_cast<unsigned>(a.K - 1),
-                  static_cast<unsigned>(batch));
-  if (sp)
-    hipLaunchKernelGGL((fwd_agg_kernel<TA, NT, EXACT, true, false>), grid, dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL((fwd_agg_kernel<TA, NT, EXACT, false, false>), grid, dim3(64), 0, s, a);
-  launch_carry(a.A, a.h0, a.ws_S, a.ws_H, nullptr, batch, a.dim, a.N, a.K, s);
-  return launch_status("ssm_scan_bwd");
-}
-
 template <typename TA, int NT, bool EXACT, bool VL>
 int launch_fwd_flags(const FwdArgs<TA>& a, int64_t batch, bool sp, bool gate, hipStream_t s) {
   if (sp)

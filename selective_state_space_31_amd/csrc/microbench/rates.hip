@@ -1,11 +1,15 @@
 // rates.hip -- gfx950 rate microbenchmarks behind the roofline figures:
-// vector fp32 FMA / MUL and v_exp_f32 issue rates at several occupancies,
-// and HBM streaming rates (copy, read, in-place update) on buffers larger
-// than the MALL.  Standalone executable; prints one line per measurement.
+// vector fp32 FMA / MUL and v_exp_f32 issue rates at several occupancies and
+// by operand kind (an SGPR operand vs VGPR operands only), the scan's
+// per-state step with the token's B/C values read from SGPRs, from VGPRs or
+// through a DPP row broadcast, and HBM streaming rates (copy, read, in-place
+// update) on buffers larger than the MALL.  Standalone executable; prints one
+// line per measurement.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
 #include <cstdlib>
+#include <utility>
 
 #define CK(x)                                                                          \
   do {                                                                                 \
@@ -29,6 +33,85 @@ __global__ void __launch_bounds__(256) k_fma(float* out, int iters, float a, flo
 #pragma unroll
   for (int i = 0; i < CH; ++i) s += v[i];
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// as k_fma with the multiplier and addend in per-lane registers (VGPRs)
+template <int CH>
+__global__ void __launch_bounds__(256) k_fma_v(float* out, int iters, float a, float b) {
+  float v[CH];
+  const float va = a + 1e-9f * threadIdx.x, vb = b + 1e-9f * threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) v[i] = 1e-3f * (i + threadIdx.x);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) v[i] = __builtin_fmaf(v[i], va, vb);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) s += v[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// The scan's per-state step over 16 states, per token: decay chain
+// d <- d*r, h <- d*h + (x*b), y <- y + c*h, with the token's b/c read
+//   SRC 0: from SGPRs (scalar loads of a row per token, as the scan does),
+//   SRC 1: from VGPRs (per-lane constants: no load, the bound without SGPRs),
+//   SRC 2: from lanes 0-15 of a VGPR through DPP row_newbcast.
+// The asm barrier keeps x*b a separate multiply, as in the scan.
+typedef const __attribute__((address_space(4))) float mb_cfloat_t;
+constexpr int kMixStates = 16, kMixTokens = 1024;
+template <int n>
+__device__ __forceinline__ float mb_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + n,
+                                                               0xF, 0xF, false));
+}
+template <int SRC, int n>
+__device__ __forceinline__ void mb_state(float (&h)[kMixStates], const float (&vb)[kMixStates],
+                                         const float (&vc)[kMixStates], mb_cfloat_t* q, float lb,
+                                         float lc, float x, float r, float& d, float& y) {
+  float b, c;
+  if constexpr (SRC == 0) { b = q[n]; c = q[kMixStates + n]; }
+  if constexpr (SRC == 1) { b = vb[n]; c = vc[n]; }
+  if constexpr (SRC == 2) { b = mb_bcast<n>(lb); c = mb_bcast<n>(lc); }
+  float u = x * b;
+  __asm__ volatile("" : "+v"(u));
+  h[n] = __builtin_fmaf(d, h[n], u);
+  y = __builtin_fmaf(c, h[n], y);
+  d *= r;
+}
+template <int SRC, int... ns>
+__device__ __forceinline__ void mb_states(std::integer_sequence<int, ns...>, float (&h)[kMixStates],
+                                          const float (&vb)[kMixStates], const float (&vc)[kMixStates],
+                                          mb_cfloat_t* q, float lb, float lc, float x, float r, float& d,
+                                          float& y) {
+  (mb_state<SRC, ns>(h, vb, vc, q, lb, lc, x, r, d, y), ...);
+}
+template <int SRC>
+__global__ void __launch_bounds__(256) k_step(float* out, const float* bc) {
+  float h[kMixStates], vb[kMixStates], vc[kMixStates];
+#pragma unroll
+  for (int n = 0; n < kMixStates; ++n) {
+    h[n] = 0.f;
+    vb[n] = 0.01f * n + 1e-7f * threadIdx.x;
+    vc[n] = 0.02f * n - 1e-7f * threadIdx.x;
+  }
+  float x = 0.3f + 1e-6f * threadIdx.x, r = 0.97f + 1e-8f * threadIdx.x, acc = 0.f;
+  const int lane = threadIdx.x & 63;
+  for (int t = 0; t < kMixTokens; ++t) {
+    const float* g = bc + (t & 63) * 2 * kMixStates;  // 64 rows of b then c
+    float lb = 0.f, lc = 0.f;
+    if constexpr (SRC == 2) {
+      lb = g[lane & 15];
+      lc = g[kMixStates + (lane & 15)];
+    }
+    r = __builtin_fmaf(r, 0.99999f, 1e-7f);
+    float d = r, y = 0.f;
+    x = __builtin_fmaf(x, 0.9999f, 1e-5f);
+    mb_states<SRC>(std::make_integer_sequence<int, kMixStates>{}, h, vb, vc, (mb_cfloat_t*)g, lb, lc,
+                   x, r, d, y);
+    acc += y;
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
 template <int CH>
@@ -137,9 +220,27 @@ int main() {
     std::printf("valu %-4s waves/SIMD=%d  %.3e lane-ops/s  %.2f lanes/clk/SIMD  %.2f clk per wave64 op\n",
                 name, waves_per_simd, rate, lanes_per_clk, 64.0 / lanes_per_clk);
   };
-  for (int w : {1, 2, 4, 8}) valu("fma", k_fma<32>, w);
+  for (int w : {1, 2, 4, 8}) valu("fma", k_fma<32>, w);  // multiplier in an SGPR
+  for (int w : {4, 8}) valu("fma-v", k_fma_v<32>, w);   // VGPR operands only
   valu("mul", k_mul<32>, 8);
   valu("exp", k_exp<32>, 8);
+  // --- per-state step, b/c from SGPRs / VGPRs / DPP broadcast
+  float* bc;
+  CK(hipMalloc(&bc, 64 * 2 * kMixStates * sizeof(float)));
+  CK(hipMemset(bc, 0, 64 * 2 * kMixStates * sizeof(float)));
+  auto step = [&](const char* name, void (*k)(float*, const float*), int waves_per_simd) {
+    const int blocks = cus * waves_per_simd;
+    const float ms = timed([&] { hipLaunchKernelGGL(k, dim3(blocks), dim3(256), 0, 0, out, bc); });
+    const double wave_tokens = static_cast<double>(blocks) * 4 * kMixTokens;
+    const double clk = ms * 1e-3 * 2.4e9 * cus * 4.0 / wave_tokens;
+    std::printf("step %-5s waves/SIMD=%d  %.1f clk per wave-token per SIMD, %.2f per state\n", name,
+                waves_per_simd, clk, clk / kMixStates);
+  };
+  for (int w : {6, 8}) {
+    step("sgpr", k_step<0>, w);
+    step("vgpr", k_step<1>, w);
+    step("dpp", k_step<2>, w);
+  }
   // --- HBM streams on 2 GiB buffers (8x the MALL)
   const size_t bytes = static_cast<size_t>(2) << 30, n = bytes / 16;
   float4 *a, *b;
