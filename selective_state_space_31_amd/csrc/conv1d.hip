@@ -29,10 +29,8 @@
 
 namespace ssm {
 
-#ifndef SSM_CONV_TOKENS
-#define SSM_CONV_TOKENS 16
-#endif
-constexpr int kConvTokens = SSM_CONV_TOKENS;  // tokens per lane in the forward
+constexpr int kConvTokens = 16;  // tokens per lane in the forward
+constexpr int kConvVecBf16 = 2;  // bf16 channels per lane and access
 
 template <typename TA>
 struct ConvArgs {
@@ -381,11 +379,8 @@ int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
         return fail(SSM_ERR_ALIAS, "%s: output %s overlaps input %s", fn, o.name, i.name);
   if (overlap(outs[0], outs[1])) return fail(SSM_ERR_ALIAS, "%s: out overlaps final_conv_state", fn);
   if (seqlen == 0 && !final_conv_state) return SSM_OK;
-  // vectors of channels where the layout allows them (bf16: 2, 4 or 8)
-#ifndef SSM_CONV_VEC_BF16
-#define SSM_CONV_VEC_BF16 2
-#endif
-  const int V = dtype == SSM_DTYPE_F32 ? 4 : SSM_CONV_VEC_BF16;
+  // vectors of channels where the layout allows them (float32: 4, bf16: 2)
+  const int V = dtype == SSM_DTYPE_F32 ? 4 : kConvVecBf16;
   const bool vec = dim % V == 0 && (seqlen == 0 || (aligned(x, V * es) && aligned(out, V * es)));
   const int64_t tiles = (dim + 64 * (vec ? V : 1) - 1) / (64 * (vec ? V : 1));
   const int64_t chunks = seqlen > 0 ? (seqlen + kConvTokens - 1) / kConvTokens : 1;
@@ -404,7 +399,7 @@ int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
                      static_cast<const bf16_t*>(initial_conv_state), static_cast<bf16_t*>(out),
                      static_cast<bf16_t*>(final_conv_state), batch, seqlen, static_cast<int>(dim),
                      0, 0};
-  return vec ? launch_conv_fwd<bf16_t, SSM_CONV_VEC_BF16>(a, static_cast<int>(width), sl, stream)
+  return vec ? launch_conv_fwd<bf16_t, kConvVecBf16>(a, static_cast<int>(width), sl, stream)
              : launch_conv_fwd<bf16_t, 1>(a, static_cast<int>(width), sl, stream);
 }
 
