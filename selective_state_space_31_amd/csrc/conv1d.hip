@@ -414,7 +414,8 @@ int ssm_causal_conv1d_update(void* conv_state, const void* x, const float* weigh
     return fail(SSM_ERR_UNSUPPORTED, "%s: silu must be 0 or 1, got %d", fn, silu);
   if (width < 2 || width > 4)
     return fail(SSM_ERR_UNSUPPORTED, "%s: width must be 2, 3 or 4, got %lld", fn, (long long)width);
-  if (batch < 1 || dim < 1 || dim > kConvMaxDim || batch * dim > (int64_t{1} << 31) - 256)
+  if (batch < 1 || dim < 1 || dim > kConvMaxDim || batch > (int64_t{1} << 31) ||
+      batch * dim > (int64_t{1} << 31) - 256)  // (batch bounded first: no overflow)
     return fail(SSM_ERR_SHAPE, "%s: bad sizes batch %lld, dim %lld", fn, (long long)batch,
                 (long long)dim);
   if (!conv_state || !x || !weight || !out)

@@ -532,8 +532,9 @@ Plan plan_fwd_chunked(int64_t batch, int64_t L, int64_t dim, int64_t N, bool var
                       int64_t chunk_len) {
   (void)varlen;
   Plan p{1, static_cast<int>(L > 0 ? L : 1), 1};
+  if (L <= 0 || chunk_len >= L) return p;  // (before rounding: chunk_len may be near INT64_MAX)
   const int64_t Lc = round_chunk(chunk_len);
-  if (L <= 0 || Lc >= L) return p;
+  if (Lc >= L) return p;
   const int64_t K = (L + Lc - 1) / Lc;
   if (K > kMaxChunks) {
     p.K = static_cast<int>(kMaxChunks + 1);
