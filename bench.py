@@ -32,9 +32,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, vendor peak
-# vector-ALU issue: a wave64 VALU instruction occupies a SIMD16 for 4 cycles,
-# so the chip issues at most 256 CUs x 4 SIMDs x 2.4 GHz / 4 wave instructions
-# per second (transcendentals take two such slots: counted twice)
+# vector-ALU issue, measured on gfx950 by the rate microbenchmark
+# (bench.py --only microbench): a wave64 VALU instruction with an SGPR
+# operand issues about once per 4.1 cycles per SIMD, one with only VGPR or
+# literal operands about once per 2.2-2.7, a transcendental once per 8.5.
+# The scan's per-state work is about half SGPR-operand instructions (the
+# token's B and C values are wave-uniform), so the issue fraction reported
+# prices every VALU instruction at 4 cycles and a transcendental at 8
+# (counted twice): 256 CUs x 4 SIMDs x 2.4 GHz / 4 wave instructions per second.
 CUS, SIMDS_PER_CU, CLOCK_HZ = 256, 4, 2.4e9
 VALU_WAVE_INSTR_PEAK = CUS * SIMDS_PER_CU * CLOCK_HZ / 4.0
 MALL_BYTES = 256 << 20      # Infinity Cache (last-level) capacity
@@ -303,8 +308,7 @@ def conv_case(name, steps, warmup, torch, ops, W):
                dtype=c["dtype"], silu=True, input_replicas=R, ms_per_step=total_ms / steps,
                kernel_ms_avg=kern_ms, **bracketed(per), algorithmic_bytes=alg,
                tokens_channels_per_s=c["batch"] * c["L"] * c["dim"] / (kern_ms * 1e-3),
-               roofline=dict(bound="hbm", achieved=round(gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                             frac=round(gbps / HBM_PEAK_GBPS, 4)))
+               roofline=roofline(name, alg, kern_ms, "one causal-conv1d call"))
     del args
     torch.cuda.empty_cache()
     return res
@@ -389,8 +393,14 @@ def ssd_case(name, steps, warmup, torch, ops, W, seed=0):
                algorithmic_flops=flops, algorithmic_bytes=alg,
                roofline_mfma=dict(bound="mfma", achieved=round(tf, 1), peak=MFMA_BF16_PEAK_TFLOPS,
                                   unit="TFLOP/s", frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4)),
-               roofline_hbm=dict(bound="hbm", achieved=round(gbps, 1), peak=HBM_PEAK_GBPS,
-                                 unit="GB/s", frac=round(gbps / HBM_PEAK_GBPS, 4)))
+               roofline_hbm=roofline(name, alg, kern_ms, "one ssm_ssd_fwd call (all its launches)"))
+    c_ = counters_entry(name)
+    if c_ is not None and c_.get("per_call", {}).get("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+        # matrix-core busy cycles (summed over the SIMDs the counter covers)
+        # over the SIMD-cycles of the call
+        busy = c_["per_call"]["SQ_VALU_MFMA_BUSY_CYCLES"]
+        res["roofline_mfma"]["mfma_busy_frac"] = round(
+            busy / (kern_ms * 1e-3 * CLOCK_HZ * CUS * SIMDS_PER_CU), 4)
     del probs, outs
     torch.cuda.empty_cache()
     return res

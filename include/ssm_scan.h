@@ -292,6 +292,11 @@ size_t ssm_ssd_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads
  * Equivalent to ssm_scan_fwd with seqlen = 1 and initial_state = last_state =
  * state.  One launch: batch * dim * (dstate / 4 when dstate % 4 == 0, else 1)
  * must stay below 2^31 - 256 (SSM_ERR_SHAPE otherwise).
+ * Alignment (SSM_ERR_ALIGN otherwise): state 16 bytes; every other array to
+ * its element size; and when dstate % 4 == 0 (each lane then updates four
+ * states with vector accesses) A 16 bytes and B, C to four elements (16
+ * bytes for float32, 8 for bf16).  Tensors from a PyTorch allocation meet
+ * all of these; views offset into one may not.
  */
 int ssm_state_update(float* state, const void* x, const void* delta, const float* delta_bias,
                      int delta_softplus, const float* A, const void* B, const void* C,

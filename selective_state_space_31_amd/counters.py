@@ -15,9 +15,10 @@ This module reads the counter-collection CSVs of those passes and writes
   * ``profiles/<workload>_counters.txt``: the same per kernel, readable.
 
 "Per call" is one call of the library entry point the workload times: the
-library's kernels (namespace ``ssm::``) summed, each kernel's total divided
-by the number of calls (the dispatch count of its least-launched kernel, as
-every call launches each of its kernels at least once).
+library's kernels (namespace ``ssm::``) summed, each counter averaged over
+the dispatches of its own pass (passes are separate runs and may make
+different numbers of calls) times the kernel's launches per call (its
+dispatch count over that of the least-launched kernel in one pass).
 
 It also turns a ``rocprofv3 --kernel-trace`` run into
 ``profiles/<workload>_kernel_stats.txt`` (per-kernel launch durations of the
@@ -79,9 +80,21 @@ def source_hash(workload):
     return h.hexdigest()[:16]
 
 
+def _waves(r):
+    """Waves a dispatch launched (Grid_Size and Workgroup_Size count work-items),
+    or None when the CSV does not give the sizes."""
+    try:
+        grid, wg = int(r["Grid_Size"]), int(r["Workgroup_Size"])
+    except (KeyError, ValueError):
+        return None
+    if wg <= 0:
+        return None
+    return (grid // wg) * ((wg + 63) // 64)
+
+
 def _rows(dirs):
-    """(dispatch id, kernel name, counter, value) of every counter-collection
-    CSV under the given rocprofv3 output directories."""
+    """(file, dispatch id, kernel name, counter, value, launched waves) of
+    every counter-collection CSV under the given rocprofv3 output directories."""
     out = []
     for d in dirs:
         files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -91,7 +104,7 @@ def _rows(dirs):
             with open(fn, newline="") as f:
                 for r in csv.DictReader(f):
                     out.append((fn, int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"],
-                                float(r["Counter_Value"])))
+                                float(r["Counter_Value"]), _waves(r)))
     return out
 
 
@@ -101,19 +114,33 @@ def _short(name):
 
 
 def per_kernel(dirs):
-    """{kernel: {"dispatches": n, counter: total}} over the library's kernels."""
-    tab = {}
-    seen = {}
-    for fn, did, kname, cname, val in _rows(dirs):
+    """Per-dispatch means over the library's kernels:
+    {kernel: {counter: mean value per dispatch}} and, per kernel, its launches
+    per call and the waves one of its dispatches launches.  Each counter is
+    averaged over the dispatches of its own pass (passes are separate runs
+    and need not make the same number of calls)."""
+    vals, waves, per_file = {}, {}, {}
+    for fn, did, kname, cname, val, wv in _rows(dirs):
         if "ssm::" not in kname:
             continue
         k = _short(kname)
-        e = tab.setdefault(k, {})
-        e[cname] = e.get(cname, 0.0) + val
-        seen.setdefault((k, cname), set()).add((fn, did))
-    for (k, cname), ids in seen.items():
-        tab[k]["dispatches"] = max(tab[k].get("dispatches", 0), len(ids))
-    return tab
+        vals.setdefault(k, {}).setdefault(cname, {})[(fn, did)] = val
+        if wv is not None:
+            waves.setdefault(k, {})[(fn, did)] = wv
+        per_file.setdefault(fn, {}).setdefault(k, set()).add(did)
+    mean = {k: {c: sum(v.values()) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
+    # launches per call from a pass that saw every kernel: dispatches of the
+    # kernel over those of the least-launched one
+    lpc = {k: 1.0 for k in mean}
+    for fn in sorted(per_file):
+        cnt = per_file[fn]
+        if set(cnt) == set(mean):
+            lo = min(len(v) for v in cnt.values())
+            lpc = {k: len(v) / lo for k, v in cnt.items()}
+            break
+    wmean = {k: sum(w.values()) / len(w) for k, w in waves.items() if w}
+    npass = {fn: min(len(v) for v in cnt.values()) for fn, cnt in per_file.items()}
+    return mean, lpc, wmean, npass
 
 
 def calibration(dirs):
@@ -121,7 +148,7 @@ def calibration(dirs):
     counters (median over its dispatches) against the bytes it moves."""
     copy_bytes = float(1 << 30)
     fetch, write = [], []
-    for _, _, kname, cname, val in _rows(dirs):
+    for _, _, kname, cname, val, _ in _rows(dirs):
         if "copy" not in kname.lower() or val <= 0:
             continue
         if cname == "FETCH_SIZE":
@@ -136,22 +163,34 @@ def calibration(dirs):
 
 
 def summarize(workload, pass_dirs, calib_dirs, command=""):
-    tab = per_kernel(pass_dirs)
-    if not tab:
+    mean, lpc, wmean, npass = per_kernel(pass_dirs)
+    if not mean:
         raise SystemExit("no library kernels in the counter passes")
     cal = calibration(calib_dirs)
-    calls = min(e["dispatches"] for e in tab.values())
     kernels = {}
     tot = {}
-    for k, e in sorted(tab.items()):
-        pc = {c: v / calls for c, v in e.items() if c != "dispatches"}
-        pc["launches_per_call"] = e["dispatches"] / calls
+    valu = trans = 0.0
+    for k in sorted(mean):
+        pc = {c: v * lpc[k] for c, v in mean[k].items()}
+        pc["launches_per_call"] = lpc[k]
+        # A check that the SQ counters saw every launched wave (they do on
+        # this part: coverage 1); instruction counts are scaled by it.
+        cov = 1.0
+        if k in wmean and mean[k].get("SQ_WAVES"):
+            pc["waves_launched"] = wmean[k] * lpc[k]
+            cov = mean[k]["SQ_WAVES"] / wmean[k]
+            pc["sq_wave_coverage"] = cov
         kernels[k] = pc
         for c, v in pc.items():
-            if c != "launches_per_call":
+            if c not in ("launches_per_call", "waves_launched", "sq_wave_coverage"):
                 tot[c] = tot.get(c, 0.0) + v
-    res = dict(workload=workload, kernel_source_sha256_16=source_hash(workload), calls_profiled=calls,
-               calibration=cal, command=command, kernels=kernels, per_call=tot)
+        if "SQ_INSTS_VALU" in pc and cov > 0:
+            valu += pc["SQ_INSTS_VALU"] / cov
+        if "SQ_INSTS_VALU_TRANS_F32" in pc and cov > 0:
+            trans += pc["SQ_INSTS_VALU_TRANS_F32"] / cov
+    res = dict(workload=workload, kernel_source_sha256_16=source_hash(workload),
+               calls_profiled=sorted(npass.values()), calibration=cal, command=command,
+               kernels=kernels, per_call=tot)
     if "FETCH_SIZE" in tot:
         res["hbm_read_bytes_per_call"] = tot["FETCH_SIZE"] * 1024.0 * cal["fetch_scale"]
     if "WRITE_SIZE" in tot:
@@ -159,9 +198,9 @@ def summarize(workload, pass_dirs, calib_dirs, command=""):
     if "FETCH_SIZE" in tot and "WRITE_SIZE" in tot:
         res["hbm_bytes_per_call"] = res["hbm_read_bytes_per_call"] + res["hbm_write_bytes_per_call"]
     if "SQ_INSTS_VALU" in tot:
-        res["valu_insts_per_call"] = tot["SQ_INSTS_VALU"]
+        res["valu_insts_per_call"] = valu  # scaled to every launched wave
     if "SQ_INSTS_VALU_TRANS_F32" in tot:
-        res["valu_trans_insts_per_call"] = tot["SQ_INSTS_VALU_TRANS_F32"]
+        res["valu_trans_insts_per_call"] = trans
     return res
 
 
@@ -172,13 +211,16 @@ def text(res):
              " -> bytes = FETCH_SIZE x 1024 x %.3f, WRITE_SIZE x 1024 x %.3f"
              % (res["calibration"]["fetch_kib"], res["calibration"]["write_kib"],
                 res["calibration"]["fetch_scale"], res["calibration"]["write_scale"]),
-             "# kernel sources hash %s; %d calls profiled" % (res["kernel_source_sha256_16"],
-                                                               res["calls_profiled"]), ""]
+             "# kernel sources hash %s; calls profiled per pass: %s" % (
+                 res["kernel_source_sha256_16"], res["calls_profiled"]), ""]
     for k, pc in res["kernels"].items():
         lines.append("== %s  (%.0f launch(es) per call)" % (k, pc["launches_per_call"]))
         for c in sorted(pc):
-            if c != "launches_per_call":
+            if c not in ("launches_per_call", "waves_launched", "sq_wave_coverage"):
                 lines.append("   %-26s %14.6g" % (c, pc[c]))
+        if "sq_wave_coverage" in pc:
+            lines.append("   -> waves launched %.0f; the SQ counters cover %.1f%% of them"
+                         % (pc["waves_launched"], 100.0 * pc["sq_wave_coverage"]))
         w = pc.get("SQ_WAVES")
         if w and "SQ_INSTS_VALU" in pc:
             tr = pc.get("SQ_INSTS_VALU_TRANS_F32")
@@ -189,6 +231,7 @@ def text(res):
     lines.append("== per call (all kernels)")
     for key in ("hbm_read_bytes_per_call", "hbm_write_bytes_per_call", "hbm_bytes_per_call",
                 "valu_insts_per_call", "valu_trans_insts_per_call"):
+        # (the VALU figures scaled to every launched wave)
         if key in res:
             lines.append("   %-26s %14.6g" % (key, res[key]))
     return "\n".join(lines) + "\n"
