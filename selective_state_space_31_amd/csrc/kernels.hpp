@@ -420,11 +420,93 @@ __device__ __forceinline__ void rows_unpack(const uint32_t* w, float (&v)[NT], b
   }
 }
 
+// B_t / C_t rows staged in LDS as float32 for the pair loop (16-bit
+// activations, 16 states).  On gfx950 a VALU instruction with an SGPR operand
+// issues at about half the rate of one whose operands are all VGPRs, and the
+// per-state input multiply and readout FMA take B_t[n] and C_t[n] as an
+// operand: read back from LDS with every lane at the same address (a
+// broadcast ds_read_b128), they arrive in VGPRs (measured on the scan's step:
+// 13.1 cycles per state against 17.8 from SGPRs at 6 waves per SIMD).
+// Each wave owns two halves of kStageTok token rows (B then C, 2*NT floats
+// per token): one half is read while the next pair of token groups' rows is
+// fetched (one 8-byte load per lane and array) and then converted into the
+// other.  A wave reads only what it wrote, and a wave's LDS accesses complete
+// in order, so no barrier is needed.
+constexpr int kStageTok = 2 * kGroup;  // tokens per half: one pair of groups
+template <typename TA, int NT>
+struct StageBC {
+  static constexpr bool OK = sizeof(TA) == 2 && NT == 16;
+  static constexpr int ROW = 2 * NT;                   // floats per token (B, C)
+  static constexpr int HALF = kStageTok * ROW;         // floats per half
+  static constexpr size_t BYTES = 2 * HALF * 4;        // per wave
+  static_assert(!OK || kStageTok * NT * 2 == 32 * 8, "one 8-byte piece per lane of a half-wave");
+  float* base;  // this wave's two halves (LDS)
+  uint32_t raw[4];  // fetched B (0, 1) and C (2, 3) words of the lane's piece
+
+  // rows of tokens [t0, t0 + kStageTok) from B and C (AGG: B only); lane l
+  // fetches 4 values of token (l % 32) / 4, states 4 (l % 4) .. + 3
+  template <bool AGG>
+  __device__ void fetch(const TA* B, const TA* C, size_t row0, int N) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t bytes = static_cast<uint32_t>(kStageTok * N) * 2;
+    const uint32_t vo = static_cast<uint32_t>(lane & 31) * 8;
+    const auto wb = __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(B + row0 * N, bytes), vo, 0, 0);
+    raw[0] = wb[0];
+    raw[1] = wb[1];
+    if constexpr (!AGG) {
+      const auto wc = __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(C + row0 * N, bytes), vo, 0, 0);
+      raw[2] = wc[0];
+      raw[3] = wc[1];
+    }
+  }
+  // the fetched rows, widened, into half `hf`: lanes 0-31 write B, 32-63 C
+  template <bool AGG>
+  __device__ void commit(int hf) const {
+    const int lane = threadIdx.x & 63;
+    const bool isC = !AGG && lane >= 32;
+    if (AGG && lane >= 32) return;
+    const uint32_t w0 = isC ? raw[2] : raw[0], w1 = isC ? raw[3] : raw[1];
+    const f32x4 v = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xffff0000u),
+                     __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xffff0000u)};
+    const int u = (lane & 31) >> 2, q = lane & 3;
+    *reinterpret_cast<f32x4*>(base + hf * HALF + u * ROW + (isC ? NT : 0) + 4 * q) = v;
+  }
+  // states 4q .. 4q+3 of token u of half hf: B (and C unless AGG), read as
+  // broadcasts
+  template <bool AGG>
+  __device__ void quad(int hf, int u, int q, float (&Bv)[4], float (&Cv)[4]) const {
+    quad_at<AGG>(base + hf * HALF + u * ROW, q, Bv, Cv);
+  }
+  // the same from a token's row address
+  template <bool AGG>
+  __device__ static void quad_at(const float* rowp, int q, float (&Bv)[4], float (&Cv)[4]) {
+    const f32x4* r = reinterpret_cast<const f32x4*>(rowp);
+    const f32x4 vb = r[q];
+    Bv[0] = vb.x;
+    Bv[1] = vb.y;
+    Bv[2] = vb.z;
+    Bv[3] = vb.w;
+    if constexpr (!AGG) {
+      const f32x4 vc = r[NT / 4 + q];
+      Cv[0] = vc.x;
+      Cv[1] = vc.y;
+      Cv[2] = vc.z;
+      Cv[3] = vc.w;
+    }
+  }
+};
+
 // Tokens [t_begin, t_begin + len) of sequence b for the wave's 64 channels.
 // AGG: summary pass (S, h); otherwise the output pass.
-template <typename TA, int NT, bool EXACT, bool SP, bool GATE, bool POW, bool AGG>
+// STG: the pair loop takes B_t / C_t from the wave's LDS staging buffer at
+// `stage` (StageBC; exact 16 states, 16-bit activations); otherwise from
+// SGPRs.
+template <typename TA, int NT, bool EXACT, bool SP, bool GATE, bool POW, bool AGG,
+          bool STG = false>
 __device__ __forceinline__ void run_tokens(const FwdArgs<TA>& a, const Chan<NT>& ch, int b,
-                                           int t_begin, int len, float (&h)[NT], float& S) {
+                                           int t_begin, int len, float (&h)[NT], float& S,
+                                           float* stage = nullptr) {
+  static_assert(!STG || (EXACT && StageBC<TA, NT>::OK), "staging: exact 16 states, 16-bit");
   using IO = Io<TA>;
   using raw_t = typename IO::raw_t;
   constexpr bool Z = GATE && !AGG;
@@ -457,7 +539,7 @@ __device__ __forceinline__ void run_tokens(const FwdArgs<TA>& a, const Chan<NT>&
   // the wait for token t's rows is followed by the loads for token t+1, and
   // scheduling barriers keep the compiler from hoisting a whole group's loads
   // (which would overflow the scalar registers into vector lanes).
-  constexpr bool PF = EXACT && NT <= 16 && (sizeof(TA) * NT) % 4 == 0;
+  constexpr bool PF = !STG && EXACT && NT <= 16 && (sizeof(TA) * NT) % 4 == 0;
   RowsRaw<TA, NT> nxt;
   if constexpr (PF) rows_load<TA, NT, AGG>(nxt, B, C);
   auto one = [&](int t, float xv, float draw, float zv) -> float {
@@ -497,7 +579,50 @@ __device__ __forceinline__ void run_tokens(const FwdArgs<TA>& a, const Chan<NT>&
   // where the buffers would only add register pressure) take the compact
   // token-at-a-time loop below for all tokens.
   int t_tail = 0;
-  if constexpr (NT <= 16 && POW) {
+  if constexpr (STG && NT <= 16 && POW) {
+    // as below, with the rows of each pair of groups from the staging buffer
+    StageBC<TA, NT> sb;
+    sb.base = stage;
+    // four states at a time, each block's rows read just ahead of it
+    auto one_st = [&](int hf, int u, float xv, float draw, float zv) -> float {
+      StepScalars st = step_begin<NT, SP, POW, false, AGG>(ch, xv, draw, S);
+#pragma unroll
+      for (int q = 0; q < NT / 4; ++q) {
+        float Bv[4], Cv[4];
+        sb.template quad<AGG>(hf, u, q, Bv, Cv);
+        step_block<NT, 4, POW, false, AGG>(h, ch, st, 4 * q, Bv, Cv);
+      }
+      return step_end<GATE, AGG>(st, zv);
+    };
+    auto compute_st = [&](int t0, int hf, int u0, const raw_t(&xs)[kGroup],
+                          const raw_t(&ds)[kGroup], const raw_t(&zs)[kGroup]) {
+      const size_t obase = (rowblk + t0) * dim + d0;
+      const rsrc_t ro = make_rsrc(a.out + (AGG ? 0 : obase), span);
+#pragma unroll
+      for (int u = 0; u < kGroup; ++u) {
+        const float y = one_st(hf, u0 + u, IO::f32(xs[u]), IO::f32(ds[u]), Z ? IO::f32(zs[u]) : 0.0f);
+        if constexpr (!AGG) IO::store(y, ro, voff_st, static_cast<uint32_t>(u) * rowbytes);
+      }
+    };
+    const int npair = len / (2 * kGroup);
+    const size_t brow = static_cast<size_t>(b) * static_cast<size_t>(a.L) + t_begin;
+    raw_t xa[kGroup], da[kGroup], za[kGroup], xb2[kGroup], db2[kGroup], zb2[kGroup];
+    // the first rows and the first group's activations in flight together
+    if (npair > 0) sb.template fetch<AGG>(a.B, a.C, brow, N);
+    fetch(0, xa, da, za);
+    if (npair > 0) sb.template commit<AGG>(0);
+    for (int i = 0; i < npair; ++i) {
+      const int t0 = i * 2 * kGroup, hf = i & 1;
+      const bool more = i + 1 < npair;
+      if (more) sb.template fetch<AGG>(a.B, a.C, brow + t0 + 2 * kGroup, N);
+      fetch(t0 + kGroup, xb2, db2, zb2);
+      compute_st(t0, hf, 0, xa, da, za);
+      fetch(t0 + 2 * kGroup, xa, da, za);
+      compute_st(t0 + kGroup, hf, kGroup, xb2, db2, zb2);
+      if (more) sb.template commit<AGG>(hf ^ 1);
+    }
+    t_tail = npair * 2 * kGroup;
+  } else if constexpr (NT <= 16 && POW) {
     const int npair = len / (2 * kGroup);
     raw_t xa[kGroup], da[kGroup], za[kGroup], xb2[kGroup], db2[kGroup], zb2[kGroup];
     fetch(0, xa, da, za);
@@ -528,9 +653,11 @@ __device__ __forceinline__ void run_tokens(const FwdArgs<TA>& a, const Chan<NT>&
 // w_n = dx_t * Q^(n+1) follows the chain w_n = w_(n-1) * Q and each state costs
 // one multiply plus one FMA whose addend operand B_t[n] is a scalar register
 // (the forward recurrence needs a third operation, dx * B, per state).
-template <typename TA, int NT, bool SP>
+template <typename TA, int NT, bool SP, bool STG = false>
 __device__ __forceinline__ void agg_reverse(const FwdArgs<TA>& a, const Chan<NT>& ch, int b,
-                                            int t_begin, int len, float (&H)[NT], float& S) {
+                                            int t_begin, int len, float (&H)[NT], float& S,
+                                            float* stage = nullptr) {
+  static_assert(!STG || StageBC<TA, NT>::OK, "staging: 16 states, 16-bit");
   using IO = Io<TA>;
   using raw_t = typename IO::raw_t;
   const int dim = a.dim, N = a.N;
@@ -550,6 +677,72 @@ __device__ __forceinline__ void agg_reverse(const FwdArgs<TA>& a, const Chan<NT>
       ds[u] = IO::load(rd, voff_ld, static_cast<uint32_t>(u) * rowbytes);
     }
   };
+  // one token's contribution given its B row supplier
+  auto step = [&](float xv, float draw, auto&& brow) {
+    const float raw = draw + ch.bias;
+    const float dt = SP ? softplus_f32(raw) : raw;
+    S += dt;
+    const float r = __builtin_amdgcn_exp2f(dt * ch.A2_0);
+    float w = dt * xv * Q;
+    brow([&](int n, float bn) {
+      H[n] = __builtin_fmaf(w, bn, H[n]);
+      w *= Q;
+    });
+    Q *= r;
+  };
+  // len is a multiple of 2*kGroup: walk pairs of groups from the end,
+  // ping-ponging two register buffers
+  raw_t xa[kGroup], da[kGroup], xb2[kGroup], db2[kGroup];
+  const int npair = len / (2 * kGroup);
+  if constexpr (STG) {
+    // B rows from the wave's staging buffer (see StageBC): the pair before
+    // the current one is fetched while the current one is walked
+    StageBC<TA, NT> sb;
+    sb.base = stage;
+    float unusedC[4];
+    // Each token's 16 accumulations are pinned in place by an empty asm that
+    // takes the states in and out: the weights w_n = dx Q^(n+1) and the rows
+    // do not depend on the state, and without the pin the compiler front-loads
+    // the loads and weights of a whole pair of groups (128 values) and sinks
+    // the accumulations, which spills.
+    auto one = [&](int hf, int u, float xv, float draw) {
+      const float* rowp = sb.base + hf * StageBC<TA, NT>::HALF + u * StageBC<TA, NT>::ROW;
+      const float raw = draw + ch.bias;
+      const float dt = SP ? softplus_f32(raw) : raw;
+      S += dt;
+      const float r = __builtin_amdgcn_exp2f(dt * ch.A2_0);
+      float w = dt * xv * Q;
+#pragma unroll
+      for (int q = 0; q < NT / 4; ++q) {
+        float Bv[4];
+        StageBC<TA, NT>::template quad_at<true>(rowp, q, Bv, unusedC);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          H[4 * q + j] = __builtin_fmaf(w, Bv[j], H[4 * q + j]);
+          w *= Q;
+        }
+      }
+      Q *= r;
+      __asm__ volatile("" : "+v"(H[0]), "+v"(H[1]), "+v"(H[2]), "+v"(H[3]), "+v"(H[4]),
+                       "+v"(H[5]), "+v"(H[6]), "+v"(H[7]), "+v"(H[8]), "+v"(H[9]), "+v"(H[10]),
+                       "+v"(H[11]), "+v"(H[12]), "+v"(H[13]), "+v"(H[14]), "+v"(H[15]));
+    };
+    if (npair > 0) sb.template fetch<true>(a.B, a.C, rowblk + (npair - 1) * 2 * kGroup, N);
+    fetch(len - kGroup, xa, da);
+    if (npair > 0) sb.template commit<true>((npair - 1) & 1);
+    for (int i = npair - 1; i >= 0; --i) {
+      const int t0 = i * 2 * kGroup, hf = i & 1;  // this pair covers [t0, t0 + 2 kGroup)
+      if (i > 0) sb.template fetch<true>(a.B, a.C, rowblk + t0 - 2 * kGroup, N);
+      fetch(t0, xb2, db2);
+#pragma unroll
+      for (int u = kGroup - 1; u >= 0; --u) one(hf, kGroup + u, IO::f32(xa[u]), IO::f32(da[u]));
+      fetch(t0 >= 2 * kGroup ? t0 - kGroup : t0, xa, da);
+#pragma unroll
+      for (int u = kGroup - 1; u >= 0; --u) one(hf, u, IO::f32(xb2[u]), IO::f32(db2[u]));
+      if (i > 0) sb.template commit<true>(hf ^ 1);
+    }
+    return;
+  }
   RowsRaw<TA, NT> nxt;
   rows_load<TA, NT, true>(nxt, B + static_cast<size_t>(len - 1) * N, B);
   auto one = [&](int t, float xv, float draw) {
@@ -559,22 +752,11 @@ __device__ __forceinline__ void agg_reverse(const FwdArgs<TA>& a, const Chan<NT>
     const size_t rn = static_cast<size_t>(t > 0 ? t - 1 : 0) * N;
     rows_load<TA, NT, true>(nxt, B + rn, B);
     __builtin_amdgcn_sched_barrier(0);
-    const float raw = draw + ch.bias;
-    const float dt = SP ? softplus_f32(raw) : raw;
-    S += dt;
-    const float r = __builtin_amdgcn_exp2f(dt * ch.A2_0);
-    float w = dt * xv * Q;
+    step(xv, draw, [&](auto&& f) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      H[n] = __builtin_fmaf(w, Bv[n], H[n]);
-      w *= Q;
-    }
-    Q *= r;
+      for (int n = 0; n < NT; ++n) f(n, Bv[n]);
+    });
   };
-  // len is a multiple of 2*kGroup: walk pairs of groups from the end,
-  // ping-ponging two register buffers
-  raw_t xa[kGroup], da[kGroup], xb2[kGroup], db2[kGroup];
-  const int npair = len / (2 * kGroup);
   fetch(len - kGroup, xa, da);
   for (int i = npair - 1; i >= 0; --i) {
     const int t0 = i * 2 * kGroup;  // this pair covers [t0, t0 + 2 kGroup)
@@ -683,6 +865,34 @@ constexpr int group_min_waves(int NT, bool EXACT) { return NT <= 16 ? (EXACT ? 6
 template <int NT>
 constexpr size_t group_lds_bytes(int G) {
   return static_cast<size_t>(G) * (NT + 1) * 64 * 4 + static_cast<size_t>(G) * 4;
+}
+// The output pass stages B_t / C_t rows in LDS (StageBC) where it can: each
+// wave's buffer follows the group slots (if any), 16-byte aligned.
+template <typename TA, int NT, bool EXACT, bool VL>
+constexpr bool out_stages_rows() { return EXACT && !VL && StageBC<TA, NT>::OK; }
+template <int NT>
+constexpr size_t stage_offset_bytes(int G, bool slots) {
+  return slots ? (group_lds_bytes<NT>(G) + 15) / 16 * 16 : 0;
+}
+// The summary pass stages B rows the same way in its reverse walk.
+template <typename TA, int NT, bool EXACT>
+constexpr bool sum_stages_rows() { return EXACT && StageBC<TA, NT>::OK; }
+// Staging pays where the walk is bound by instruction issue: chunks of at
+// least kStageMinChunk tokens (measured: -4% on 512-token chunks, -5% on
+// 256-token chunks; +5% on 32-token chunks, whose short walks are bound by
+// latency, which the LDS reads add to every token).
+constexpr int kStageMinChunk = 128;
+template <typename TA, int NT, bool EXACT, bool STG>
+constexpr size_t sum_lds_bytes(int G) {
+  return STG && sum_stages_rows<TA, NT, EXACT>()
+             ? stage_offset_bytes<NT>(G, true) + static_cast<size_t>(G) * StageBC<TA, NT>::BYTES
+             : group_lds_bytes<NT>(G);
+}
+template <typename TA, int NT, bool EXACT, bool VL, bool STG>
+constexpr size_t out_lds_bytes(int G, bool slots) {
+  return STG && out_stages_rows<TA, NT, EXACT, VL>()
+             ? stage_offset_bytes<NT>(G, slots) + static_cast<size_t>(G) * StageBC<TA, NT>::BYTES
+             : (slots ? group_lds_bytes<NT>(G) : 0);
 }
 
 // Calls f(n, exp(A[d,n] S)) for the lane's channel, n = 0 .. NT-1 (ACC: each
@@ -805,7 +1015,8 @@ struct WsSlot {
 
 // Summary pass: block (channel tile, group j, sequence b) of G waves; wave w
 // summarises chunk c = j G + w (c <= K-2; the others carry the identity).
-template <typename TA, int NT, bool EXACT, bool SP, bool VL>
+// STG: B rows staged in LDS (see StageBC, kStageMinChunk).
+template <typename TA, int NT, bool EXACT, bool SP, bool VL, bool STG>
 __global__ void __launch_bounds__(64 * group_max(NT, EXACT), group_min_waves(NT, EXACT))
     fwd_sum_kernel(FwdArgs<TA> a) {
   constexpr bool ACC = sizeof(TA) == 4;
@@ -846,8 +1057,15 @@ __global__ void __launch_bounds__(64 * group_max(NT, EXACT), group_min_waves(NT,
     if (!reset) {
       constexpr bool REV = EXACT && NT <= 16 && sizeof(TA) == 2 && (sizeof(TA) * NT) % 4 == 0;
       if (ch.pow) {
-        if constexpr (REV)
-          agg_reverse<TA, NT, SP>(a, ch, b, t_begin, a.Lc, H, S);
+        if constexpr (REV) {
+          constexpr bool ST = STG && sum_stages_rows<TA, NT, EXACT>();
+          float* stage = nullptr;
+          if constexpr (ST) {
+            extern __shared__ float dyn_lds[];
+            stage = dyn_lds + stage_offset_bytes<NT>(G, true) / 4 + w * (StageBC<TA, NT>::BYTES / 4);
+          }
+          agg_reverse<TA, NT, SP, ST>(a, ch, b, t_begin, a.Lc, H, S, stage);
+        }
         else
           run_tokens<TA, NT, EXACT, SP, false, true, true>(a, ch, b, t_begin, a.Lc, H, S);
       } else {
@@ -922,7 +1140,7 @@ __global__ void __launch_bounds__(64 * group_max(NT, EXACT), group_min_waves(NT,
 // chunk is walked segment by segment (the parts of it that belong to one
 // sequence): the state is reset at each sequence start and stored to
 // last_state at each sequence end.  K == 1: one wave per block, no prologue.
-template <typename TA, int NT, bool EXACT, bool SP, bool GATE, bool VL>
+template <typename TA, int NT, bool EXACT, bool SP, bool GATE, bool VL, bool STG>
 __global__ void __launch_bounds__(64 * group_max(NT, EXACT), group_min_waves(NT, EXACT))
     fwd_out_kernel(FwdArgs<TA> a) {
   constexpr bool ACC = sizeof(TA) == 4;
@@ -1013,10 +1231,16 @@ __global__ void __launch_bounds__(64 * group_max(NT, EXACT), group_min_waves(NT,
   const int t_begin = c * a.Lc;
   const int len = (a.L - t_begin < a.Lc) ? a.L - t_begin : a.Lc;
   float S = 0.0f;
+  constexpr bool ST = STG && out_stages_rows<TA, NT, EXACT, VL>();
+  float* stage = nullptr;
+  if constexpr (ST) {
+    extern __shared__ float dyn_lds[];
+    stage = dyn_lds + stage_offset_bytes<NT>(G, a.K > 1) / 4 + w * (StageBC<TA, NT>::BYTES / 4);
+  }
   if constexpr (!VL) {
     if (len > 0) {  // an empty sequence only carries the initial state through
       if (ch.pow)
-        run_tokens<TA, NT, EXACT, SP, GATE, true, false>(a, ch, b, t_begin, len, h, S);
+        run_tokens<TA, NT, EXACT, SP, GATE, true, false, ST>(a, ch, b, t_begin, len, h, S, stage);
       else
         run_tokens<TA, NT, EXACT, SP, GATE, false, false>(a, ch, b, t_begin, len, h, S);
     }
@@ -1056,7 +1280,7 @@ __global__ void __launch_bounds__(64 * group_max(NT, EXACT), group_min_waves(NT,
       if (e <= t) e = t + 1;  // (offsets not sorted: still move on)
       if (st == t) load_h0<NT, EXACT>(a.h0, s, a.dim, dl, N, h);
       if (ch.pow)
-        run_tokens<TA, NT, EXACT, SP, GATE, true, false>(a, ch, 0, t, e - t, h, S);
+        run_tokens<TA, NT, EXACT, SP, GATE, true, false, ST>(a, ch, 0, t, e - t, h, S, stage);
       else
         run_tokens<TA, NT, EXACT, SP, GATE, false, false>(a, ch, 0, t, e - t, h, S);
       if (e == en) {
@@ -1086,25 +1310,27 @@ void launch_varlen_empty(const int* cu, int nseq, const float* h0, float* last_s
 // Lets a kernel take `bytes` of dynamic LDS (once per kernel); 0 or an error.
 int allow_dynamic_lds(const void* kernel, size_t bytes);
 
-template <typename TA, int NT, bool EXACT, bool SP, bool GATE, bool VL>
-int launch_fwd(const FwdArgs<TA>& a, int64_t batch, hipStream_t s) {
+template <typename TA, int NT, bool EXACT, bool SP, bool GATE, bool VL, bool STG>
+int launch_fwd_as(const FwdArgs<TA>& a, int64_t batch, hipStream_t s) {
   const unsigned tiles = static_cast<unsigned>((a.dim + 63) / 64);
   const char* fn = VL ? "ssm_scan_fwd_varlen" : "ssm_scan_fwd";
   const int G = a.K > 1 ? a.G : 1;
-  const size_t lds = a.K > 1 ? group_lds_bytes<NT>(G) : 0;
+  const size_t lds = a.K > 1 ? sum_lds_bytes<TA, NT, EXACT, STG>(G) : 0;
+  const size_t lds_out = out_lds_bytes<TA, NT, EXACT, VL, STG>(G, a.K > 1);
+  const void* ko =
+      reinterpret_cast<const void*>(&fwd_out_kernel<TA, NT, EXACT, SP, GATE, VL, STG>);
+  if (allow_dynamic_lds(ko, lds_out) != 0) return launch_status(fn);
   if (a.K > 1) {
-    const void* ks = reinterpret_cast<const void*>(&fwd_sum_kernel<TA, NT, EXACT, SP, VL>);
-    const void* ko = reinterpret_cast<const void*>(&fwd_out_kernel<TA, NT, EXACT, SP, GATE, VL>);
-    if (allow_dynamic_lds(ks, lds) != 0 || allow_dynamic_lds(ko, lds) != 0)
-      return launch_status(fn);
+    const void* ks = reinterpret_cast<const void*>(&fwd_sum_kernel<TA, NT, EXACT, SP, VL, STG>);
+    if (allow_dynamic_lds(ks, lds) != 0) return launch_status(fn);
     const unsigned kga = static_cast<unsigned>((a.K - 1 + G - 1) / G);
-    hipLaunchKernelGGL((fwd_sum_kernel<TA, NT, EXACT, SP, VL>),
+    hipLaunchKernelGGL((fwd_sum_kernel<TA, NT, EXACT, SP, VL, STG>),
                        dim3(tiles, kga, static_cast<unsigned>(batch)), dim3(64 * G), lds, s, a);
   }
   if (!VL || a.L > 0) {
     const unsigned kg = static_cast<unsigned>((a.K + G - 1) / G);
-    hipLaunchKernelGGL((fwd_out_kernel<TA, NT, EXACT, SP, GATE, VL>),
-                       dim3(tiles, kg, static_cast<unsigned>(batch)), dim3(64 * G), lds, s, a);
+    hipLaunchKernelGGL((fwd_out_kernel<TA, NT, EXACT, SP, GATE, VL, STG>),
+                       dim3(tiles, kg, static_cast<unsigned>(batch)), dim3(64 * G), lds_out, s, a);
   }
   // no tokens at all: every packed sequence's last_state is its initial state
   // (otherwise the output pass stores those of the empty ones)
@@ -1113,8 +1339,15 @@ int launch_fwd(const FwdArgs<TA>& a, int64_t batch, hipStream_t s) {
   return launch_status(fn);
 }
 
-// The state entering every chunk (summary and carry passes only; ws_H slot
-// c holds it for c >= 1 afterwards), for the backward's recomputation.
+// Staged rows (StageBC) for chunks of at least kStageMinChunk tokens.
+template <typename TA, int NT, bool EXACT, bool SP, bool GATE, bool VL>
+int launch_fwd(const FwdArgs<TA>& a, int64_t batch, hipStream_t s) {
+  if constexpr (EXACT && StageBC<TA, NT>::OK) {
+    if (a.Lc >= kStageMinChunk) return launch_fwd_as<TA, NT, EXACT, SP, GATE, VL, true>(a, batch, s);
+  }
+  return launch_fwd_as<TA, NT, EXACT, SP, GATE, VL, false>(a, batch, s);
+}
+
 template <typename TA, int NT, bool EXACT, bool VL>
 int launch_fwd_flags(const FwdArgs<TA>& a, int64_t batch, bool sp, bool gate, hipStream_t s) {
   if (sp)
