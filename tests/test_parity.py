@@ -239,22 +239,25 @@ def test_limit_cumsum(dtype):
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_chunk_plans_agree(dtype, A_kind):
     """One input under several time splits (the library's own, 8-token
-    chunks, 24-token chunks, one chunk per sequence): every result matches
-    the oracle, and the splits match each other within twice the tolerance
-    (each is within one tolerance of the exact result).  A carry or LDS race
-    would show up here as a split-dependent result."""
+    chunks, 24-token chunks, 128- and 200-token chunks, one chunk per
+    sequence): every result matches the oracle, and the splits match each
+    other within twice the tolerance (each is within one tolerance of the
+    exact result).  A carry or LDS race would show up here as a
+    split-dependent result.  Chunks of 128 tokens and more take the B/C rows
+    from the LDS staging buffers (bf16, S4D-real A); 777 tokens leave ragged
+    last chunks (9 and 177 tokens: a pair of token groups plus a tail)."""
     p = make_problem(2, 777, 96, 16, dtype=dtype, gate=True, seed=34, device=DEV, A_kind=A_kind,
                      initial_state=True)
     ref, ref_last = oracle_for(p)
     rtol, atol = TOL[dtype]
     res = {}
-    for cl in (0, 8, 24, 777):
+    for cl in (0, 8, 24, 128, 200, 777):
         print("case: chunk_len", cl, dtype, A_kind, flush=True)
         out, last = ssm_scan_fwd_chunked(**p.tensors(), chunk_len=cl, return_last_state=True)
         torch.cuda.synchronize()
         assert_close(to_np(out), ref, rtol, atol, "chunk_len %d out" % cl)
         assert_close(to_np(last), ref_last, rtol, atol, "chunk_len %d last_state" % cl)
         res[cl] = (to_np(out), to_np(last))
-    for cl in (8, 24, 777):
+    for cl in (8, 24, 128, 200, 777):
         assert_close(res[cl][0], res[0][0], 2 * rtol, 2 * atol, "chunk_len %d vs default" % cl)
         assert_close(res[cl][1], res[0][1], 2 * rtol, 2 * atol, "chunk_len %d vs default last" % cl)

@@ -139,6 +139,17 @@ def test_no_last_state_requested():
     assert_close(to_np(out), ref, *TOL["fp32"], what="out only")
 
 
+def test_long_chunks_with_staged_rows():
+    """A wide layer (96 channel tiles) over 16.4k packed tokens: the plan cuts
+    chunks of more than 128 tokens, where the summary pass reads B from the
+    LDS staging buffers; sequence starts fall inside chunks (summarised from
+    the start, not staged) and between them."""
+    lengths = [7000, 3, 2500, 0, 1700, 5217]
+    p = make_varlen_problem(lengths, 6144, 16, dtype="bf16", gate=True, seed=41, device=DEV,
+                            initial_state=True)
+    run_and_compare(p, "long chunks, staged rows")
+
+
 def test_config_varlen_mamba130m_bf16_full():
     c = VARLEN_CONFIGS["varlen_mamba130m_bf16"]
     lengths = varlen_lengths(c["total"], c["len_range"], seed=0)
