@@ -238,6 +238,15 @@ __device__ __forceinline__ f32x4* a2_table() {
   __shared__ f32x4 tab[NT / 4 * 64];
   return tab;
 }
+// The same table for the per-token reads: volatile (read every token, never
+// hoisted out of the token loop) through an LDS-qualified pointer, so they
+// are ds_read_b128 (a volatile access through a generic pointer stays a flat
+// load, which also waits on the vector memory counter).
+typedef const volatile __attribute__((address_space(3))) f32x4 lds_table_t;
+template <int NT>
+__device__ __forceinline__ lds_table_t* a2_table_rd() {
+  return (lds_table_t*)a2_table<NT>();
+}
 
 template <int NT>
 struct Chan {
@@ -346,7 +355,7 @@ __device__ __forceinline__ void step_block(float (&h)[NT], const Chan<NT>& ch, S
     // read per token, never hoisted out of the token loop); the scheduling
     // barrier keeps the compiler from lifting all N exponentials ahead of
     // their uses, which would hold N more values per lane.
-    const volatile f32x4* tab = a2_table<NT>();
+    lds_table_t* tab = a2_table_rd<NT>();
 #pragma unroll
     for (int q = 0; q < NB / 4; ++q) {
       const f32x4 v = tab[(n0 / 4 + q) * 64 + (threadIdx.x & 63)];
@@ -355,7 +364,11 @@ __device__ __forceinline__ void step_block(float (&h)[NT], const Chan<NT>& ch, S
       for (int j = 0; j < 4; ++j) {
         const int n = n0 + 4 * q + j;
         const float dA = __builtin_amdgcn_exp2f(s.dt * a2[j]);
-        fma_inplace(h[n], dA, s.dx * Bv[4 * q + j]);
+        // decay, then the input term accumulated into h: both in h's own
+        // register (in the one-token loop the form a*h + (dx*B) had its
+        // result land in the product's register and be copied back)
+        h[n] *= dA;
+        h[n] = __builtin_fmaf(s.dx, Bv[4 * q + j], h[n]);
         if constexpr (!AGG) s.y = __builtin_fmaf(Cv[4 * q + j], h[n], s.y);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -918,7 +931,7 @@ __device__ __forceinline__ void for_decays(const Chan<NT>& ch, float S, Fn f) {
       }
     }
   } else {
-    const volatile f32x4* tab = a2_table<NT>();
+    lds_table_t* tab = a2_table_rd<NT>();
 #pragma unroll
     for (int q = 0; q < NT / 4; ++q) {
       const f32x4 v = tab[q * 64 + (threadIdx.x & 63)];
