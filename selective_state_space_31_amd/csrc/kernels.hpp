@@ -351,15 +351,17 @@ __device__ __forceinline__ void step_block(float (&h)[NT], const Chan<NT>& ch, S
       if constexpr (!AGG) s.y = __builtin_fmaf(Cv[j], h[n], s.y);
     }
   } else {
-    // Four states at a time, exponents read from the LDS table (volatile:
-    // read per token, never hoisted out of the token loop); the scheduling
-    // barrier keeps the compiler from lifting all N exponentials ahead of
-    // their uses, which would hold N more values per lane.
+    // Exponents from the LDS table (volatile: read per token, never hoisted
+    // out of the token loop), the block's reads issued together, and the
+    // exponentials left free to interleave with the updates, so that neither
+    // a table read nor an exponential is waited for right after its issue.
     lds_table_t* tab = a2_table_rd<NT>();
+    f32x4 a2q[NB / 4];
+#pragma unroll
+    for (int q = 0; q < NB / 4; ++q) a2q[q] = tab[(n0 / 4 + q) * 64 + (threadIdx.x & 63)];
 #pragma unroll
     for (int q = 0; q < NB / 4; ++q) {
-      const f32x4 v = tab[(n0 / 4 + q) * 64 + (threadIdx.x & 63)];
-      const float a2[4] = {v.x, v.y, v.z, v.w};
+      const float a2[4] = {a2q[q].x, a2q[q].y, a2q[q].z, a2q[q].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int n = n0 + 4 * q + j;
@@ -371,7 +373,6 @@ __device__ __forceinline__ void step_block(float (&h)[NT], const Chan<NT>& ch, S
         h[n] = __builtin_fmaf(s.dx, Bv[4 * q + j], h[n]);
         if constexpr (!AGG) s.y = __builtin_fmaf(Cv[4 * q + j], h[n], s.y);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
