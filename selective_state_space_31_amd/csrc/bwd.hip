@@ -40,6 +40,7 @@
 namespace ssm {
 
 constexpr int kBwdStripe = 32;     // tokens per stripe at most (a multiple of 16)
+constexpr int kAdjGroup = 4;      // tokens per load group of the adjoint summary walk
 constexpr int kBwdThreads = 256;   // main pass workgroup: 4 waves of the same stripe
 
 // Main-pass shape for a state width: SPL states per lane, G lanes per
@@ -116,13 +117,28 @@ __device__ __forceinline__ void bwd_agg_block(const BwdArgs<TA>& a, int tile, in
   const int s = c * a.Ls;
   const int e = (s + a.Ls < a.L) ? s + a.Ls : a.L;
   float S = 0.0f;
-  auto token = [&](int t, float& dt, float& dy, float (&Cv)[NT]) {
+  // A token's inputs: its dt and dy inputs (per lane) and its C row (uniform).
+  // The walks take tokens in groups of kAdjGroup whose loads are all issued
+  // before the first of them is used, so a group waits for memory once.
+  struct Tok {
+    TA dl, g, zz;
+    float Cv[NT];
+  };
+  auto fetch = [&](int t, Tok& k) {
     const size_t i = (static_cast<size_t>(b) * a.L + t) * a.dim + dl;
-    const float u = to_f32(a.delta[i]) + bias;
+    k.dl = a.delta[i];
+    k.g = a.dout[i];
+    if constexpr (GATE) k.zz = a.z[i];
+    load_row<NT, true>(a.C + (static_cast<size_t>(b) * a.L + t) * NT, NT, k.Cv);
+  };
+  auto prep = [&](const Tok& k, float& dt, float& dy) {
+    const float u = to_f32(k.dl) + bias;
     dt = SP ? softplus_f32(u) : u;
-    const float g = to_f32(a.dout[i]);
-    dy = GATE ? g * silu_f32(to_f32(a.z[i])) : g;
-    load_row<NT, true>(a.C + (static_cast<size_t>(b) * a.L + t) * NT, NT, Cv);
+    const float g = to_f32(k.g);
+    if constexpr (GATE)
+      dy = g * silu_f32(to_f32(k.zz));
+    else
+      dy = g;
   };
   // The summary is sum_t (prod_{u=s..t} e^(dt_u A)) C_t dy_t.  S4D-real A
   // (every lane of the wave): e^(dt A[n]) = r^(n+1), r = e^(dt A[0]), so walking
@@ -132,26 +148,42 @@ __device__ __forceinline__ void bwd_agg_block(const BwdArgs<TA>& a, int tile, in
   // backwards, a <- (a + C_t dy_t) e^(dt_t A), one exponential per state.
   if (pw) {
     float P = 1.0f;
-    for (int t = s; t < e; ++t) {
-      float dt, dy, Cv[NT];
-      token(t, dt, dy, Cv);
-      S += dt;
-      P *= __builtin_amdgcn_exp2f(dt * a2[0]);
-      float wgt = dy * P;
+    for (int t0 = s; t0 < e; t0 += kAdjGroup) {
+      Tok k[kAdjGroup];
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        adj[n] = __builtin_fmaf(wgt, Cv[n], adj[n]);
-        wgt *= P;
+      for (int u = 0; u < kAdjGroup; ++u) fetch(t0 + u < e ? t0 + u : e - 1, k[u]);
+#pragma unroll
+      for (int u = 0; u < kAdjGroup; ++u) {
+        if (t0 + u < e) {
+          float dt, dy;
+          prep(k[u], dt, dy);
+          S += dt;
+          P *= __builtin_amdgcn_exp2f(dt * a2[0]);
+          float wgt = dy * P;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            adj[n] = __builtin_fmaf(wgt, k[u].Cv[n], adj[n]);
+            wgt *= P;
+          }
+        }
       }
     }
   } else {
-    for (int t = e - 1; t >= s; --t) {
-      float dt, dy, Cv[NT];
-      token(t, dt, dy, Cv);
-      S += dt;
+    for (int t1 = e; t1 > s; t1 -= kAdjGroup) {  // tokens t1-1 down to t1-kAdjGroup
+      Tok k[kAdjGroup];
 #pragma unroll
-      for (int n = 0; n < NT; ++n)
-        adj[n] = __builtin_fmaf(Cv[n], dy, adj[n]) * __builtin_amdgcn_exp2f(dt * a2[n]);
+      for (int u = 0; u < kAdjGroup; ++u) fetch(t1 - 1 - u >= s ? t1 - 1 - u : s, k[u]);
+#pragma unroll
+      for (int u = 0; u < kAdjGroup; ++u) {
+        if (t1 - 1 - u >= s) {
+          float dt, dy;
+          prep(k[u], dt, dy);
+          S += dt;
+#pragma unroll
+          for (int n = 0; n < NT; ++n)
+            adj[n] = __builtin_fmaf(k[u].Cv[n], dy, adj[n]) * __builtin_amdgcn_exp2f(dt * a2[n]);
+        }
+      }
     }
   }
   if (valid) {
