@@ -83,6 +83,26 @@ def test_shapes(shape, dtype):
     run_and_compare(p, what="shape %s %s" % (shape, dtype))
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("N", [1, 4, 5, 8, 12, 16, 32, 64])
+def test_general_A_state_widths(N, dtype):
+    """A non-structured A (every decay its own exponential, read from the
+    exponent table) at every state width the kernels are built for, exact
+    and padded: the library's plan (32-token chunks in groups) and 200-token
+    chunks with a ragged last one.  (With N = 1 every A has the S4D-real
+    shape.)"""
+    p = make_problem(1, 1000, 70, N, dtype=dtype, gate=True, seed=300 + N, device=DEV,
+                     A_kind="general", initial_state=True)
+    ref, ref_last = oracle_for(p)
+    rtol, atol = TOL[dtype]
+    for cl in (0, 200):
+        print("case: general A, N", N, dtype, "chunk_len", cl, flush=True)
+        out, last = ssm_scan_fwd_chunked(**p.tensors(), chunk_len=cl, return_last_state=True)
+        torch.cuda.synchronize()
+        assert_close(to_np(out), ref, rtol, atol, "general A N=%d chunk_len %d out" % (N, cl))
+        assert_close(to_np(last), ref_last, rtol, atol, "general A N=%d chunk_len %d last" % (N, cl))
+
+
 FLAGS = [
     dict(gate=False), dict(with_D=False), dict(with_bias=False), dict(delta_softplus=False),
     dict(initial_state=False), dict(A_kind="general"), dict(A_kind="general", gate=False),
