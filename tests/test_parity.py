@@ -65,6 +65,17 @@ def test_config_longctx_bf16_sampled():
     run_and_compare(p, None, torch.from_numpy(d_idx).to(DEV), what="longctx_bf16 sampled")
 
 
+def test_config_longctx_bf16_general_A_sampled():
+    """The 131k-token layer with a non-structured (trained-like) A: every
+    decay its own exponential over memories of up to 10^4 steps, in the
+    plan's 512-token chunks; sampled channels against the oracle."""
+    c = CONFIGS["longctx_bf16"]
+    p = make_problem(**c, seed=5, device=DEV, engine="torch_cuda", A_kind="general")
+    rng = np.random.default_rng(3)
+    d_idx = np.unique(np.concatenate([[0, 63, 64, c["dim"] - 1], rng.choice(c["dim"], 28, replace=False)]))
+    run_and_compare(p, None, torch.from_numpy(d_idx).to(DEV), what="longctx_bf16 general A sampled")
+
+
 SHAPES = [
     # (batch, L, dim, N)
     (1, 1, 64, 16), (2, 3, 64, 16), (1, 63, 64, 16), (1, 64, 64, 16), (1, 65, 64, 16),
