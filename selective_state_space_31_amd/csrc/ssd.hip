@@ -150,13 +150,23 @@ __device__ __forceinline__ bf16x8 cat8(s16x4 lo, s16x4 hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// XOR swizzles of the 16-byte piece index of an LDS row (they change only
-// the low three bits, i.e. the bank group within 128 bytes).
-//  B, C rows: bits 1 and 2 of (row % 8) swapped.  Eight consecutive rows
-//    get distinct pieces (row reads of the products are conflict free), and
-//    rows 4i..4i+3 get {0,1,4,5} or {2,3,6,7}: with the alternating 8-byte
-//    halves of the state tiles (below) the transpose loads of B^T are too.
+// XOR swizzles of the 16-byte piece index of an LDS row.  The LDS has 64
+// banks of 4 bytes (256 bytes per cycle: a wave's 16-byte reads take 4
+// cycles when conflict free).
+//  B, C rows: bits 1 and 2 of (row % 8) swapped in the low three bits, so
+//    eight consecutive rows get distinct pieces, and rows 4i..4i+3 get
+//    {0,1,4,5} or {2,3,6,7}.  With 128 states (256-byte rows) the 128-byte
+//    half is also flipped by bit 3 of the row (half_bc), so that the 16
+//    rows a wave's operand reads cover (16 consecutive rows for the
+//    products, rows 8q + 0..3 (+4) for the transposes of B^T) fall on all 64
+//    banks rather than 32 or 16 of them.  Measured per wave-instruction:
+//    the B^T transposes 8.5 -> 4.5 cycles, the 16-byte row reads of the
+//    products 8.1 -> 4.5.
 __device__ __forceinline__ int swz_bc(int r) { return (r & 1) | ((r & 2) << 1) | ((r & 4) >> 1); }
+template <bool ON>
+__device__ __forceinline__ int half_bc(int r) {
+  return ON ? 128 * ((r >> 3) & 1) : 0;
+}
 //  x rows (128 bytes): 2 (row % 4) + bit 2 of the row, for the transpose loads of X^T.
 __device__ __forceinline__ int swz_x(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
 //  S rows (128 bytes): row % 8.
@@ -174,12 +184,19 @@ __device__ __forceinline__ int nmap(int nb, int q) {
   return 32 * (nb >> 1) + 8 * q + 4 * ((nb & 1) ^ (q & 1));
 }
 
+// Row-read offset of k-step kk (16 states: pieces 4 kk + q) from the bases
+// of the two piece parities: the 128-byte half by an XOR, which keeps the
+// row's own half flip (half_bc) in place.
+__device__ __forceinline__ int bc_off(const int (&bc_kp)[2], int kk) {
+  return bc_kp[kk & 1] ^ (128 * (kk >> 1));
+}
+
 // Tiles (sb, tb0..tb0+NTB-1) of S^T (rows s in 16 sb, columns t in 16 tb):
 // S^T = B C^T masked and scaled, written to sS as S[t][s] in bf16.
 template <int NS, int NTB>
 __device__ __forceinline__ void ssd_s_tiles(const unsigned char* sB, const unsigned char* sC,
                                             unsigned char* sS, const float* slam,
-                                            const float* sdt, const int (&bc_base)[2], int lane,
+                                            const float* sdt, const int (&bc_kp)[2], int lane,
                                             int sb, int tb0) {
   constexpr int RB = NS * 2;
   const int m = lane & 15, q = lane >> 4;
@@ -188,7 +205,7 @@ __device__ __forceinline__ void ssd_s_tiles(const unsigned char* sB, const unsig
   for (int i = 0; i < NTB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < NS / 32; ++kk) {
-    const int off = bc_base[kk & 1] + 128 * (kk >> 1);
+    const int off = bc_off(bc_kp, kk);
     const bf16x8 av = lds_b128(sB, off + 16 * RB * sb);
 #pragma unroll
     for (int i = 0; i < NTB; ++i) {
@@ -237,6 +254,8 @@ ssd_fwd_kernel(SsdArgs a) {
   constexpr int NBC = Q * PPR / kSsdThreads;   // B (and C) pieces per thread
   constexpr int RPJ = kSsdThreads / PPR;       // rows between a thread's B / C pieces
   constexpr int NX = Q * P / 8 / kSsdThreads;  // x pieces per thread
+  constexpr bool SWZH = RB == 256;  // the 128-byte half flipped by row bit 3 (half_bc)
+  constexpr int NH = SWZH ? 2 : 1;  // B^T transpose bases per 128-byte half
   static_assert(RPJ % 8 == 0 && NX == 2, "layout");
   __shared__ __attribute__((aligned(16))) unsigned char sB[Q * RB];
   // C and S share one region: once every wave has formed its products, the
@@ -315,9 +334,12 @@ ssd_fwd_kernel(SsdArgs a) {
   // per-lane offsets (loop constants)
   const uint32_t vo_bc = (tid / PPR) * rowBC + (tid % PPR) * 16;
   // B and C rows: the two 8-byte halves of every odd 16-byte piece are
-  // stored swapped (see the state tiles' n mapping)
-  const int lds_bc = (tid / PPR) * RB + (((tid % PPR) ^ swz_bc((tid / PPR) & 7)) << 4);
-  const int lds_bc_lo = lds_bc + 8 * (tid & 1), lds_bc_hi = lds_bc + 8 * (1 - (tid & 1));
+  // stored swapped (see the state tiles' n mapping); each thread writes
+  // whole 16-byte pieces (as two 8-byte halves the writes conflicted 4-way)
+  static_assert(!SWZH || RPJ % 16 == 0, "a thread's rows share bit 3");
+  const int lds_bc = (tid / PPR) * RB +
+                     ((((tid % PPR) ^ swz_bc((tid / PPR) & 7)) << 4) ^ half_bc<SWZH>(tid / PPR));
+  const bool bc_odd = (tid & 1) != 0;  // (PPR is even: the piece's parity)
   const uint32_t vo_x = (tid >> 3) * rowX + (tid & 7) * 16;
   const int lds_x = (tid >> 3) * 128 + (((tid & 7) ^ swz_x(tid >> 3)) << 4);
   // z, out: whole 128-byte rows; lane -> token 16 w + 8 i + lane / 8, channels 8 (lane % 8) .. +7
@@ -326,22 +348,23 @@ ssd_fwd_kernel(SsdArgs a) {
   // LDS address bases of the operand reads; the loop indices (k-step, row
   // block, tile) enter as immediate offsets
   const int k4 = m >> 2, bq = m & 3;
-  int bc_base[2];  // B, C rows 16 blk + m, pieces 4 kk + q (kk parity kp)
+  int bc_kp[2];   // B, C rows 16 blk + m, pieces 4 kk + q (kk parity kp), first half
   int s_base[2];   // S rows 16 tb + m, pieces 4 kk + q
 #pragma unroll
-  for (int kp = 0; kp < 2; ++kp) {
-    bc_base[kp] = m * RB + (((4 * kp + q) ^ swz_bc(m & 7)) << 4);
-    s_base[kp] = m * 128 + (((4 * kp + q) ^ swz_s(m)) << 4);
-  }
+  for (int kp = 0; kp < 2; ++kp)
+    bc_kp[kp] = m * RB + ((((4 * kp + q) ^ swz_bc(m & 7)) << 4) ^ half_bc<SWZH>(m));
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp) s_base[kp] = m * 128 + (((4 * kp + q) ^ swz_s(m)) << 4);
   const int x_ep = m * 128 + (((2 * w + (q >> 1)) ^ swz_x(m)) << 4) + 8 * (q & 1);
   int xt_base[2];        // X^T transpose loads: rows 32 kk + 8 q + k4 + 4 f
-  int bt_base[2][2];     // B^T transpose loads: [f][tile pair parity]
+  int bt_base[2][2];  // B^T transpose loads: [f][tile pair parity], first 128-byte half
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     const int r = 8 * q + k4 + 4 * f;
     xt_base[f] = r * 128 + (((2 * w + (bq >> 1)) ^ swz_x(r)) << 4) + 8 * (bq & 1);
 #pragma unroll
-    for (int c1 = 0; c1 < 2; ++c1) bt_base[f][c1] = r * RB + (((4 * c1 + bq) ^ swz_bc(r & 7)) << 4);
+    for (int c1 = 0; c1 < 2; ++c1)
+      bt_base[f][c1] = r * RB + ((((4 * c1 + bq) ^ swz_bc(r & 7)) << 4) ^ half_bc<SWZH>(r));
   }
 
   u32x4 pb[NBC], pc[NBC], px[NX];
@@ -408,11 +431,11 @@ ssd_fwd_kernel(SsdArgs a) {
 #pragma unroll
     for (int j = 0; j < NBC; ++j) {
       const int o = j * RPJ * RB;
-      *reinterpret_cast<u32x2*>(sB + lds_bc_lo + o) = u32x2{pb[j][0], pb[j][1]};
-      *reinterpret_cast<u32x2*>(sB + lds_bc_hi + o) = u32x2{pb[j][2], pb[j][3]};
+      *reinterpret_cast<u32x4*>(sB + lds_bc + o) =
+          bc_odd ? u32x4{pb[j][2], pb[j][3], pb[j][0], pb[j][1]} : pb[j];
       if constexpr (FULL) {
-        *reinterpret_cast<u32x2*>(sC + lds_bc_lo + o) = u32x2{pc[j][0], pc[j][1]};
-        *reinterpret_cast<u32x2*>(sC + lds_bc_hi + o) = u32x2{pc[j][2], pc[j][3]};
+        *reinterpret_cast<u32x4*>(sC + lds_bc + o) =
+            bc_odd ? u32x4{pc[j][2], pc[j][3], pc[j][0], pc[j][1]} : pc[j];
       }
     }
 #pragma unroll
@@ -444,16 +467,16 @@ ssd_fwd_kernel(SsdArgs a) {
       // (the two zero tiles are rewritten every chunk: the outputs staged
       // at the end of a chunk may cover S)
       if (w == 0) {
-        ssd_s_tiles<NS, 3>(sB, sC, sS, slam, sdt, bc_base, lane, 0, 0);
+        ssd_s_tiles<NS, 3>(sB, sC, sS, slam, sdt, bc_kp, lane, 0, 0);
         ssd_s_zero(sS, lane, 1, 0);
       } else if (w == 1) {
-        ssd_s_tiles<NS, 3>(sB, sC, sS, slam, sdt, bc_base, lane, 1, 1);
+        ssd_s_tiles<NS, 3>(sB, sC, sS, slam, sdt, bc_kp, lane, 1, 1);
       } else if (w == 2) {
-        ssd_s_tiles<NS, 2>(sB, sC, sS, slam, sdt, bc_base, lane, 2, 2);
+        ssd_s_tiles<NS, 2>(sB, sC, sS, slam, sdt, bc_kp, lane, 2, 2);
         ssd_s_zero(sS, lane, 3, 2);
       } else {
-        ssd_s_tiles<NS, 1>(sB, sC, sS, slam, sdt, bc_base, lane, 0, 3);
-        ssd_s_tiles<NS, 1>(sB, sC, sS, slam, sdt, bc_base, lane, 3, 3);
+        ssd_s_tiles<NS, 1>(sB, sC, sS, slam, sdt, bc_kp, lane, 0, 3);
+        ssd_s_tiles<NS, 1>(sB, sC, sS, slam, sdt, bc_kp, lane, 3, 3);
       }
       // bf16 copy of the entering state as the A operand of H C^T: lane (q, m)
       // holds h[16 w + m][n] for the n of its tiles 2 kk, 2 kk + 1 in that order
@@ -476,7 +499,7 @@ ssd_fwd_kernel(SsdArgs a) {
           y1 = mfma16(xa[kk], lds_b128(sS, s_base[kk] + 16 * 128 * tb), y1);
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk)
-          y2 = mfma16(hA[kk], lds_b128(sC, bc_base[kk & 1] + 128 * (kk >> 1) + 16 * RB * tb), y2);
+          y2 = mfma16(hA[kk], lds_b128(sC, bc_off(bc_kp, kk) + 16 * RB * tb), y2);
       };
       // y before the gate: lane (q, m) holds channels 16 w + 4 q .. +3 of token 16 tb + m
       auto combine = [&](int tb, const f32x4& y1, const f32x4& y2) {
@@ -526,9 +549,11 @@ ssd_fwd_kernel(SsdArgs a) {
       if constexpr (!FULL) lam_seg += slam[Q - 1] * kLn2;
       // A operands (B^T) of tile nb for both k-steps, read one tile ahead
       auto bt_read = [&](int nb, int kk) {
-        const int imm = 32 * RB * kk + 128 * (nb >> 2) + 8 * (nb & 1);
-        const int c1 = (nb >> 1) & 1;
-        return cat8(lds_tr(sB, bt_base[0][c1] + imm), lds_tr(sB, bt_base[1][c1] + imm));
+        // (one base per 128-byte half when the half is flipped per row,
+        // else the half is an immediate offset)
+        const int imm = 32 * RB * kk + 8 * (nb & 1) + (NH == 1 ? 128 * (nb >> 2) : 0);
+        const int c1 = (nb >> 1) & 1, hx = NH == 2 ? 128 * (nb >> 2) : 0;
+        return cat8(lds_tr(sB, (bt_base[0][c1] ^ hx) + imm), lds_tr(sB, (bt_base[1][c1] ^ hx) + imm));
       };
       bf16x8 an0 = bt_read(0, 0), an1 = bt_read(0, 1);
 #pragma unroll

@@ -164,3 +164,22 @@ def test_config_ssd_mamba2_2p7b_bf16_sampled_heads():
     p = make_ssd_problem(**c, seed=0, device=DEV, engine="torch_cuda")
     heads = torch.tensor([0, 1, 37, 79], device=DEV)
     run_and_compare(p, "ssd_mamba2_2p7b_bf16 (4 heads)", heads=heads)
+
+
+def test_bitwise_deterministic_full_size():
+    """The 2.7B-shaped layer (4 segments per sequence, every workgroup slot
+    in use) six times: every output and final state bit for bit equal and
+    finite.  An ordering fault between the waves of a workgroup would show
+    as run-to-run differences here."""
+    c = SSD_CONFIGS["ssd_mamba2_2p7b_bf16"]
+    p = make_ssd_problem(**c, seed=7, device=DEV, engine="torch_cuda")
+    first = None
+    for run in range(6):
+        out, last = ssm_ssd_fwd(p.x, p.dt, p.A, p.B, p.C, D=p.D, z=p.z, dt_bias=p.dt_bias,
+                                dt_softplus=p.dt_softplus, return_last_state=True)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all() and torch.isfinite(last).all(), "run %d" % run
+        if first is None:
+            first = (out, last)
+        else:
+            assert torch.equal(out, first[0]) and torch.equal(last, first[1]), "run %d differs" % run

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from selective_state_space_31_amd import SsmError, ssm_scan_fwd
+from selective_state_space_31_amd import SsmError, ssm_scan_fwd, ssm_scan_fwd_chunked
 from selective_state_space_31_amd.workloads import make_problem
 from tests._helpers import TOL, assert_close, to_np
 
@@ -36,6 +36,22 @@ def test_bitwise_deterministic():
     o2, l2 = ssm_scan_fwd(**p.tensors(), return_last_state=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_bitwise_deterministic_staged_long_chunks():
+    """A plan of 512-token chunks in groups (the long-context layer's), whose
+    summary and output walks take B/C from the LDS staging buffers: three
+    runs bit for bit equal."""
+    p = make_problem(1, 32768, 2048, 16, dtype="bf16", gate=False, seed=44, device=DEV,
+                     engine="torch_cuda")
+    first = None
+    for _ in range(3):
+        o, l = ssm_scan_fwd_chunked(**p.tensors(), chunk_len=512, return_last_state=True)
+        torch.cuda.synchronize()
+        if first is None:
+            first = (o, l)
+        else:
+            assert torch.equal(o, first[0]) and torch.equal(l, first[1])
 
 
 def test_causal():
