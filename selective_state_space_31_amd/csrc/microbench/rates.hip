@@ -2,9 +2,10 @@
 // vector fp32 FMA / MUL and v_exp_f32 issue rates at several occupancies and
 // by operand kind (an SGPR operand vs VGPR operands only), the scan's
 // per-state step with the token's B/C values read from SGPRs, from VGPRs or
-// through a DPP row broadcast, and HBM streaming rates (copy, read, in-place
-// update) on buffers larger than the MALL.  Standalone executable; prints one
-// line per measurement.
+// through a DPP row broadcast, LDS access patterns of the SSD kernel's B/C
+// rows (bank conflicts: the 64 banks of 4 bytes, 256 bytes per cycle), and
+// HBM streaming rates (copy, read, in-place update) on buffers larger than
+// the MALL.  Standalone executable; prints one line per measurement.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -144,6 +145,78 @@ __global__ void __launch_bounds__(256) k_exp(float* out, int iters, float, float
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// --- LDS access patterns.  Per-lane byte offsets of the SSD kernel's B/C
+// rows (64 rows of 256 bytes: 128 bf16 states per token), for one wave
+// instruction each (index i), in the earlier layout (the 16-byte piece index
+// XOR-swizzled by the row within each 128-byte half) and the current one
+// (the half also flipped by bit 3 of the row).
+__device__ __forceinline__ int lds_swz(int r) { return (r & 1) | ((r & 2) << 1) | ((r & 4) >> 1); }
+template <int P>
+__device__ int lds_addr(int lane, int tid, int i) {
+  const int m = lane & 15, q = lane >> 4, k4 = m >> 2, bq = m & 3;
+  if (P == 0 || P == 1) return (lane * 8 + i * 512) & 16383;  // contiguous 8 bytes per lane
+  if (P == 4) return (lane * 16 + i * 1024) & 16383;          // contiguous 16 bytes per lane
+  if (P == 2 || P == 3) {  // B^T transposes (tr16_b64): i = 4 tile + 2 k-step + f
+    const int nb = i >> 2, kk = (i >> 1) & 1, f = i & 1;
+    const int r = 8 * q + k4 + 4 * f, piece = (4 * ((nb >> 1) & 1) + bq) ^ lds_swz(r & 7);
+    const int hb = (nb >> 2) ^ (P == 3 ? (r >> 3) & 1 : 0);
+    return r * 256 + 32 * 256 * kk + 128 * hb + piece * 16 + 8 * (nb & 1);
+  }
+  if (P == 5 || P == 6) {  // 16-byte row reads of the products: i = 4 k-step + row block
+    const int kk = (i >> 2) & 3, sb = i & 3, row = 16 * sb + m;
+    const int piece = (4 * (kk & 1) + q) ^ lds_swz(m & 7);
+    const int hb = (kk >> 1) ^ (P == 6 ? (row >> 3) & 1 : 0);
+    return row * 256 + 128 * hb + piece * 16;
+  }
+  // staging writes of the rows: thread tid owns piece tid % 16 of rows tid / 16 + 16 j
+  const int j = P == 7 ? (i >> 1) & 3 : i & 3, row = tid / 16 + 16 * j;
+  const int piece = ((tid % 16) ^ lds_swz(row & 7)) ^ (P == 8 ? 8 * ((row >> 3) & 1) : 0);
+  return row * 256 + piece * 16 + (P == 7 ? 8 * ((i & 1) ^ (tid & 1)) : 0);
+}
+template <int P>
+constexpr int lds_n() { return (P == 5 || P == 6) ? 16 : (P == 7 ? 8 : (P == 8 ? 4 : 32)); }
+typedef __attribute__((ext_vector_type(4))) short lds_s16x4_t;
+typedef __attribute__((address_space(3))) lds_s16x4_t lds_tr_t;
+typedef __attribute__((ext_vector_type(2))) unsigned lds_u2_t;
+typedef __attribute__((ext_vector_type(4))) unsigned lds_u4_t;
+typedef __attribute__((address_space(3))) volatile lds_u2_t lds_u2_p;
+typedef __attribute__((address_space(3))) volatile lds_u4_t lds_u4_p;
+template <int P>
+__global__ void __launch_bounds__(256) k_lds(float* out, int iters) {
+  __shared__ __attribute__((aligned(16))) unsigned char buf[32768];
+  for (int i = threadIdx.x; i < 8192; i += 256) reinterpret_cast<unsigned*>(buf)[i] = i * 2654435761u;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  constexpr int N = lds_n<P>();
+  int a[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) a[i] = lds_addr<P>(lane, threadIdx.x, i);
+  unsigned acc = 0;
+  for (int it = 0; it < iters; ++it) {
+    const int off = (it & 1) << 14;  // alternate the two 16 KB halves (the same banks)
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if constexpr (P == 1 || P == 2 || P == 3) {
+        const lds_s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr_t*)(buf + a[i] + off));
+        acc += static_cast<unsigned>(v[0]) ^ static_cast<unsigned>(v[3]);
+      } else if constexpr (P == 0) {
+        const lds_u2_t v = *(lds_u2_p*)(buf + a[i] + off);
+        acc += v[0] ^ v[1];
+      } else if constexpr (P == 7) {
+        *(lds_u2_p*)(buf + a[i] + off) = lds_u2_t{acc, acc + 1u};
+        acc += 3u;
+      } else if constexpr (P == 8) {
+        *(lds_u4_p*)(buf + a[i] + off) = lds_u4_t{acc, acc + 1u, acc + 2u, acc + 3u};
+        acc += 5u;
+      } else {
+        const lds_u4_t v = *(lds_u4_p*)(buf + a[i] + off);
+        acc += v[0] ^ v[3];
+      }
+    }
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = static_cast<float>(acc & 1u);
+}
+
 __global__ void __launch_bounds__(256) k_copy(const float4* __restrict__ in, float4* __restrict__ out,
                                               size_t n) {
   const size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
@@ -241,6 +314,23 @@ int main() {
     step("vgpr", k_step<1>, w);
     step("dpp", k_step<2>, w);
   }
+  // --- LDS access patterns: cycles of one CU per wave instruction
+  auto lds = [&](const char* name, void (*k)(float*, int), int n) {
+    const int blocks = cus * 8, iters = 2000;
+    const float ms = timed([&] { hipLaunchKernelGGL(k, dim3(blocks), dim3(256), 0, 0, out, iters); });
+    const double inst_per_cu = blocks * 4.0 / cus * iters * n;
+    std::printf("lds  %-52s %6.2f clk per wave-instruction per CU\n", name,
+                ms * 1e-3 * 2.4e9 / inst_per_cu);
+  };
+  lds("read b64, contiguous", k_lds<0>, lds_n<0>());
+  lds("read tr16_b64, contiguous", k_lds<1>, lds_n<1>());
+  lds("read tr16_b64, B^T of the SSD, earlier layout", k_lds<2>, lds_n<2>());
+  lds("read tr16_b64, B^T of the SSD, half flipped by row bit 3", k_lds<3>, lds_n<3>());
+  lds("read b128, contiguous", k_lds<4>, lds_n<4>());
+  lds("read b128, SSD product rows, earlier layout", k_lds<5>, lds_n<5>());
+  lds("read b128, SSD product rows, half flipped by row bit 3", k_lds<6>, lds_n<6>());
+  lds("write b64, SSD row staging in 8-byte halves (earlier)", k_lds<7>, lds_n<7>());
+  lds("write b128, SSD row staging in 16-byte pieces (current)", k_lds<8>, lds_n<8>());
   // --- HBM streams on 2 GiB buffers (8x the MALL)
   const size_t bytes = static_cast<size_t>(2) << 30, n = bytes / 16;
   float4 *a, *b;
