@@ -185,15 +185,17 @@ __device__ __forceinline__ int nmap(int nb, int q) {
 }
 
 // Row-read offset of k-step kk (16 states: pieces 4 kk + q) from the bases
-// of the two piece parities: the 128-byte half by an XOR, which keeps the
-// row's own half flip (half_bc) in place.
+// of the two piece parities.  With the half flip (half_bc) the 128-byte half
+// is selected by an XOR, which keeps the row's own flip; without it, by an
+// addition (which the compiler folds into the instruction's offset).
+template <bool SWZH>
 __device__ __forceinline__ int bc_off(const int (&bc_kp)[2], int kk) {
-  return bc_kp[kk & 1] ^ (128 * (kk >> 1));
+  return SWZH ? bc_kp[kk & 1] ^ (128 * (kk >> 1)) : bc_kp[kk & 1] + 128 * (kk >> 1);
 }
 
 // Tiles (sb, tb0..tb0+NTB-1) of S^T (rows s in 16 sb, columns t in 16 tb):
 // S^T = B C^T masked and scaled, written to sS as S[t][s] in bf16.
-template <int NS, int NTB>
+template <int NS, int NTB, bool SWZH>
 __device__ __forceinline__ void ssd_s_tiles(const unsigned char* sB, const unsigned char* sC,
                                             unsigned char* sS, const float* slam,
                                             const float* sdt, const int (&bc_kp)[2], int lane,
@@ -205,7 +207,7 @@ __device__ __forceinline__ void ssd_s_tiles(const unsigned char* sB, const unsig
   for (int i = 0; i < NTB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < NS / 32; ++kk) {
-    const int off = bc_off(bc_kp, kk);
+    const int off = bc_off<SWZH>(bc_kp, kk);
     const bf16x8 av = lds_b128(sB, off + 16 * RB * sb);
 #pragma unroll
     for (int i = 0; i < NTB; ++i) {
@@ -254,7 +256,12 @@ ssd_fwd_kernel(SsdArgs a) {
   constexpr int NBC = Q * PPR / kSsdThreads;   // B (and C) pieces per thread
   constexpr int RPJ = kSsdThreads / PPR;       // rows between a thread's B / C pieces
   constexpr int NX = Q * P / 8 / kSsdThreads;  // x pieces per thread
-  constexpr bool SWZH = RB == 256;  // the 128-byte half flipped by row bit 3 (half_bc)
+  // The 128-byte half of the B/C rows flipped by row bit 3 (half_bc): in the
+  // state pass.  The output pass keeps the halves in place: at its register
+  // limit the flip's extra address registers spilled, and the reloads, which
+  // wait for every outstanding load, cost more than the conflicts they
+  // remove once the inputs come from HBM (same box: 127 -> 130 us).
+  constexpr bool SWZH = RB == 256 && !FULL;
   constexpr int NH = SWZH ? 2 : 1;  // B^T transpose bases per 128-byte half
   static_assert(RPJ % 8 == 0 && NX == 2, "layout");
   __shared__ __attribute__((aligned(16))) unsigned char sB[Q * RB];
@@ -467,16 +474,16 @@ ssd_fwd_kernel(SsdArgs a) {
       // (the two zero tiles are rewritten every chunk: the outputs staged
       // at the end of a chunk may cover S)
       if (w == 0) {
-        ssd_s_tiles<NS, 3>(sB, sC, sS, slam, sdt, bc_kp, lane, 0, 0);
+        ssd_s_tiles<NS, 3, SWZH>(sB, sC, sS, slam, sdt, bc_kp, lane, 0, 0);
         ssd_s_zero(sS, lane, 1, 0);
       } else if (w == 1) {
-        ssd_s_tiles<NS, 3>(sB, sC, sS, slam, sdt, bc_kp, lane, 1, 1);
+        ssd_s_tiles<NS, 3, SWZH>(sB, sC, sS, slam, sdt, bc_kp, lane, 1, 1);
       } else if (w == 2) {
-        ssd_s_tiles<NS, 2>(sB, sC, sS, slam, sdt, bc_kp, lane, 2, 2);
+        ssd_s_tiles<NS, 2, SWZH>(sB, sC, sS, slam, sdt, bc_kp, lane, 2, 2);
         ssd_s_zero(sS, lane, 3, 2);
       } else {
-        ssd_s_tiles<NS, 1>(sB, sC, sS, slam, sdt, bc_kp, lane, 0, 3);
-        ssd_s_tiles<NS, 1>(sB, sC, sS, slam, sdt, bc_kp, lane, 3, 3);
+        ssd_s_tiles<NS, 1, SWZH>(sB, sC, sS, slam, sdt, bc_kp, lane, 0, 3);
+        ssd_s_tiles<NS, 1, SWZH>(sB, sC, sS, slam, sdt, bc_kp, lane, 3, 3);
       }
       // bf16 copy of the entering state as the A operand of H C^T: lane (q, m)
       // holds h[16 w + m][n] for the n of its tiles 2 kk, 2 kk + 1 in that order
@@ -499,7 +506,7 @@ ssd_fwd_kernel(SsdArgs a) {
           y1 = mfma16(xa[kk], lds_b128(sS, s_base[kk] + 16 * 128 * tb), y1);
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk)
-          y2 = mfma16(hA[kk], lds_b128(sC, bc_off(bc_kp, kk) + 16 * RB * tb), y2);
+          y2 = mfma16(hA[kk], lds_b128(sC, bc_off<SWZH>(bc_kp, kk) + 16 * RB * tb), y2);
       };
       // y before the gate: lane (q, m) holds channels 16 w + 4 q .. +3 of token 16 tb + m
       auto combine = [&](int tb, const f32x4& y1, const f32x4& y2) {
