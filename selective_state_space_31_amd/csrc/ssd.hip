@@ -150,22 +150,23 @@ __device__ __forceinline__ bf16x8 cat8(s16x4 lo, s16x4 hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// XOR swizzles of the 16-byte piece index of an LDS row.  The LDS has 64
-// banks of 4 bytes (256 bytes per cycle: a wave's 16-byte reads take 4
-// cycles when conflict free).
-//  B, C rows: bits 1 and 2 of (row % 8) swapped in the low three bits, so
-//    eight consecutive rows get distinct pieces, and rows 4i..4i+3 get
-//    {0,1,4,5} or {2,3,6,7}.  With 128 states (256-byte rows) the 128-byte
-//    half is also flipped by bit 3 of the row (half_bc), so that the 16
-//    rows a wave's operand reads cover (16 consecutive rows for the
-//    products, rows 8q + 0..3 (+4) for the transposes of B^T) fall on all 64
-//    banks rather than 32 or 16 of them.  Measured per wave-instruction:
-//    the B^T transposes 8.5 -> 4.5 cycles, the 16-byte row reads of the
-//    products 8.1 -> 4.5.
+// LDS layout of the B and C rows (token rows of NS bf16 states): rows of 128
+// bytes, 64 states each, so that consecutive rows fall on the two halves of
+// the 64 banks of 4 bytes (256 bytes per cycle); with 128 states the row's
+// second 64 states are in a second plane of Q such rows (kBcPlane bytes
+// further), which the operand reads reach by an immediate offset.  (Rows of
+// 256 bytes all start at bank 0: a wave's transpose loads of B^T and 16-byte
+// row reads then fell on a quarter to a half of the banks, 8.1 cycles per
+// wave instruction against 4.4 now.)  The 16-byte pieces of a 128-byte row
+// are XOR-swizzled by the row: bits 1 and 2 of (row % 8) swapped, so eight
+// consecutive rows get distinct pieces, and rows 4i..4i+3 get {0,1,4,5} or
+// {2,3,6,7}.
+constexpr int kBcRow = 128;                 // bytes per row of a plane
+constexpr int kBcPlane = kSsdQ * kBcRow;    // bytes per plane
 __device__ __forceinline__ int swz_bc(int r) { return (r & 1) | ((r & 2) << 1) | ((r & 4) >> 1); }
-template <bool ON>
-__device__ __forceinline__ int half_bc(int r) {
-  return ON ? 128 * ((r >> 3) & 1) : 0;
+// byte offset of the 16-byte piece P (states 8P..8P+7) of row r
+__device__ __forceinline__ int bc_addr(int r, int P) {
+  return (P >> 3) * kBcPlane + r * kBcRow + (((P & 7) ^ swz_bc(r & 7)) << 4);
 }
 //  x rows (128 bytes): 2 (row % 4) + bit 2 of the row, for the transpose loads of X^T.
 __device__ __forceinline__ int swz_x(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
@@ -185,33 +186,29 @@ __device__ __forceinline__ int nmap(int nb, int q) {
 }
 
 // Row-read offset of k-step kk (16 states: pieces 4 kk + q) from the bases
-// of the two piece parities.  With the half flip (half_bc) the 128-byte half
-// is selected by an XOR, which keeps the row's own flip; without it, by an
-// addition (which the compiler folds into the instruction's offset).
-template <bool SWZH>
+// of the two piece parities in the first plane.
 __device__ __forceinline__ int bc_off(const int (&bc_kp)[2], int kk) {
-  return SWZH ? bc_kp[kk & 1] ^ (128 * (kk >> 1)) : bc_kp[kk & 1] + 128 * (kk >> 1);
+  return bc_kp[kk & 1] + kBcPlane * (kk >> 1);
 }
 
 // Tiles (sb, tb0..tb0+NTB-1) of S^T (rows s in 16 sb, columns t in 16 tb):
 // S^T = B C^T masked and scaled, written to sS as S[t][s] in bf16.
-template <int NS, int NTB, bool SWZH>
+template <int NS, int NTB>
 __device__ __forceinline__ void ssd_s_tiles(const unsigned char* sB, const unsigned char* sC,
                                             unsigned char* sS, const float* slam,
                                             const float* sdt, const int (&bc_kp)[2], int lane,
                                             int sb, int tb0) {
-  constexpr int RB = NS * 2;
   const int m = lane & 15, q = lane >> 4;
   f32x4 acc[NTB];
 #pragma unroll
   for (int i = 0; i < NTB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < NS / 32; ++kk) {
-    const int off = bc_off<SWZH>(bc_kp, kk);
-    const bf16x8 av = lds_b128(sB, off + 16 * RB * sb);
+    const int off = bc_off(bc_kp, kk);
+    const bf16x8 av = lds_b128(sB, off + 16 * kBcRow * sb);
 #pragma unroll
     for (int i = 0; i < NTB; ++i) {
-      const bf16x8 bv = lds_b128(sC, off + 16 * RB * (tb0 + i));
+      const bf16x8 bv = lds_b128(sC, off + 16 * kBcRow * (tb0 + i));
       acc[i] = mfma16(av, bv, acc[i]);
     }
   }
@@ -256,13 +253,7 @@ ssd_fwd_kernel(SsdArgs a) {
   constexpr int NBC = Q * PPR / kSsdThreads;   // B (and C) pieces per thread
   constexpr int RPJ = kSsdThreads / PPR;       // rows between a thread's B / C pieces
   constexpr int NX = Q * P / 8 / kSsdThreads;  // x pieces per thread
-  // The 128-byte half of the B/C rows flipped by row bit 3 (half_bc): in the
-  // state pass.  The output pass keeps the halves in place: at its register
-  // limit the flip's extra address registers spilled, and the reloads, which
-  // wait for every outstanding load, cost more than the conflicts they
-  // remove once the inputs come from HBM (same box: 127 -> 130 us).
-  constexpr bool SWZH = RB == 256 && !FULL;
-  constexpr int NH = SWZH ? 2 : 1;  // B^T transpose bases per 128-byte half
+  static_assert(RB <= 2 * kBcRow, "B/C rows span at most two planes");
   static_assert(RPJ % 8 == 0 && NX == 2, "layout");
   __shared__ __attribute__((aligned(16))) unsigned char sB[Q * RB];
   // C and S share one region: once every wave has formed its products, the
@@ -343,9 +334,7 @@ ssd_fwd_kernel(SsdArgs a) {
   // B and C rows: the two 8-byte halves of every odd 16-byte piece are
   // stored swapped (see the state tiles' n mapping); each thread writes
   // whole 16-byte pieces (as two 8-byte halves the writes conflicted 4-way)
-  static_assert(!SWZH || RPJ % 16 == 0, "a thread's rows share bit 3");
-  const int lds_bc = (tid / PPR) * RB +
-                     ((((tid % PPR) ^ swz_bc((tid / PPR) & 7)) << 4) ^ half_bc<SWZH>(tid / PPR));
+  const int lds_bc = bc_addr(tid / PPR, tid % PPR);
   const bool bc_odd = (tid & 1) != 0;  // (PPR is even: the piece's parity)
   const uint32_t vo_x = (tid >> 3) * rowX + (tid & 7) * 16;
   const int lds_x = (tid >> 3) * 128 + (((tid & 7) ^ swz_x(tid >> 3)) << 4);
@@ -359,7 +348,7 @@ ssd_fwd_kernel(SsdArgs a) {
   int s_base[2];   // S rows 16 tb + m, pieces 4 kk + q
 #pragma unroll
   for (int kp = 0; kp < 2; ++kp)
-    bc_kp[kp] = m * RB + ((((4 * kp + q) ^ swz_bc(m & 7)) << 4) ^ half_bc<SWZH>(m));
+    bc_kp[kp] = bc_addr(m, 4 * kp + q);
 #pragma unroll
   for (int kp = 0; kp < 2; ++kp) s_base[kp] = m * 128 + (((4 * kp + q) ^ swz_s(m)) << 4);
   const int x_ep = m * 128 + (((2 * w + (q >> 1)) ^ swz_x(m)) << 4) + 8 * (q & 1);
@@ -371,7 +360,7 @@ ssd_fwd_kernel(SsdArgs a) {
     xt_base[f] = r * 128 + (((2 * w + (bq >> 1)) ^ swz_x(r)) << 4) + 8 * (bq & 1);
 #pragma unroll
     for (int c1 = 0; c1 < 2; ++c1)
-      bt_base[f][c1] = r * RB + ((((4 * c1 + bq) ^ swz_bc(r & 7)) << 4) ^ half_bc<SWZH>(r));
+      bt_base[f][c1] = bc_addr(r, 4 * c1 + bq);
   }
 
   u32x4 pb[NBC], pc[NBC], px[NX];
@@ -437,7 +426,7 @@ ssd_fwd_kernel(SsdArgs a) {
     // ---- 1. stage the chunk fetched ahead; wave 0 forms lambda and the weights ----
 #pragma unroll
     for (int j = 0; j < NBC; ++j) {
-      const int o = j * RPJ * RB;
+      const int o = j * RPJ * kBcRow;
       *reinterpret_cast<u32x4*>(sB + lds_bc + o) =
           bc_odd ? u32x4{pb[j][2], pb[j][3], pb[j][0], pb[j][1]} : pb[j];
       if constexpr (FULL) {
@@ -474,16 +463,16 @@ ssd_fwd_kernel(SsdArgs a) {
       // (the two zero tiles are rewritten every chunk: the outputs staged
       // at the end of a chunk may cover S)
       if (w == 0) {
-        ssd_s_tiles<NS, 3, SWZH>(sB, sC, sS, slam, sdt, bc_kp, lane, 0, 0);
+        ssd_s_tiles<NS, 3>(sB, sC, sS, slam, sdt, bc_kp, lane, 0, 0);
         ssd_s_zero(sS, lane, 1, 0);
       } else if (w == 1) {
-        ssd_s_tiles<NS, 3, SWZH>(sB, sC, sS, slam, sdt, bc_kp, lane, 1, 1);
+        ssd_s_tiles<NS, 3>(sB, sC, sS, slam, sdt, bc_kp, lane, 1, 1);
       } else if (w == 2) {
-        ssd_s_tiles<NS, 2, SWZH>(sB, sC, sS, slam, sdt, bc_kp, lane, 2, 2);
+        ssd_s_tiles<NS, 2>(sB, sC, sS, slam, sdt, bc_kp, lane, 2, 2);
         ssd_s_zero(sS, lane, 3, 2);
       } else {
-        ssd_s_tiles<NS, 1, SWZH>(sB, sC, sS, slam, sdt, bc_kp, lane, 0, 3);
-        ssd_s_tiles<NS, 1, SWZH>(sB, sC, sS, slam, sdt, bc_kp, lane, 3, 3);
+        ssd_s_tiles<NS, 1>(sB, sC, sS, slam, sdt, bc_kp, lane, 0, 3);
+        ssd_s_tiles<NS, 1>(sB, sC, sS, slam, sdt, bc_kp, lane, 3, 3);
       }
       // bf16 copy of the entering state as the A operand of H C^T: lane (q, m)
       // holds h[16 w + m][n] for the n of its tiles 2 kk, 2 kk + 1 in that order
@@ -506,7 +495,7 @@ ssd_fwd_kernel(SsdArgs a) {
           y1 = mfma16(xa[kk], lds_b128(sS, s_base[kk] + 16 * 128 * tb), y1);
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk)
-          y2 = mfma16(hA[kk], lds_b128(sC, bc_off<SWZH>(bc_kp, kk) + 16 * RB * tb), y2);
+          y2 = mfma16(hA[kk], lds_b128(sC, bc_off(bc_kp, kk) + 16 * kBcRow * tb), y2);
       };
       // y before the gate: lane (q, m) holds channels 16 w + 4 q .. +3 of token 16 tb + m
       auto combine = [&](int tb, const f32x4& y1, const f32x4& y2) {
@@ -556,11 +545,10 @@ ssd_fwd_kernel(SsdArgs a) {
       if constexpr (!FULL) lam_seg += slam[Q - 1] * kLn2;
       // A operands (B^T) of tile nb for both k-steps, read one tile ahead
       auto bt_read = [&](int nb, int kk) {
-        // (one base per 128-byte half when the half is flipped per row,
-        // else the half is an immediate offset)
-        const int imm = 32 * RB * kk + 8 * (nb & 1) + (NH == 1 ? 128 * (nb >> 2) : 0);
-        const int c1 = (nb >> 1) & 1, hx = NH == 2 ? 128 * (nb >> 2) : 0;
-        return cat8(lds_tr(sB, (bt_base[0][c1] ^ hx) + imm), lds_tr(sB, (bt_base[1][c1] ^ hx) + imm));
+        // (tiles nb >= 4 hold states 64..127: the second plane)
+        const int imm = 32 * kBcRow * kk + 8 * (nb & 1) + kBcPlane * (nb >> 2);
+        const int c1 = (nb >> 1) & 1;
+        return cat8(lds_tr(sB, bt_base[0][c1] + imm), lds_tr(sB, bt_base[1][c1] + imm));
       };
       bf16x8 an0 = bt_read(0, 0), an1 = bt_read(0, 1);
 #pragma unroll
